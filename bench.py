@@ -1,0 +1,186 @@
+"""Throughput of the block predictor's hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of the workload:
+project_kv_block (the step's new blocks), project_q, score_blocks and
+rank_victims (see rank_kv_block_amd/workloads.py).  The default workload is the
+Llama-3-8B-shaped decode step: 32 layers x 8192 blocks, 2 GiB of A_g per step.
+
+Prints one JSON line.  `value` is the A_g bytes the step's scoring reads per
+second of whole-step time, in GB/s; the score kernel alone is timed with HIP
+events on the stream it runs on and reported in `roofline`.  The oracle's time
+on a bounded sample of the same work, on this host's cores, is `cpu_baseline`.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, 8 TB/s
+
+
+def _score_kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ["score_decode.hip", "common.h", "kernels.h"]:
+        with open(os.path.join(ROOT, "rank_kv_block_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload, launch_bytes):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the current kernel."""
+    path = os.path.join(ROOT, "profiles", f"score_decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != _score_kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s=15.0):
+    """The oracle as it stands, on the GPU's own q_proj and A_g of as many scored
+    (layer, sequence) rows as fit in ~budget_s seconds of host time."""
+    import numpy as np
+    import torch
+    from oracle import predictor
+    from tests.devmem import a_g_layer
+
+    c = wl.cfg
+    qp_all = wl.q_proj.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    q_all = wl.q.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    import rank_kv_block_amd as rk
+    P = rk.pred_copy_projection(wl.h)
+    phys = wl.phys.numpy()
+    l0 = wl.layer0_for_step(0)
+    rows = 0
+    blocks = 0
+    elapsed = 0.0
+    for li in range(c.step_layers):
+        a_layer = a_g_layer(wl.h, wl.d, l0 + li)
+        for s in range(c.S):
+            slots = np.ascontiguousarray(a_layer[phys[s]])
+            t0 = time.perf_counter()
+            predictor.project_q(q_all[l0 + li, s], P)
+            sc = predictor.score_one(qp_all[li, s], slots)
+            predictor.rank_victims(sc.astype(np.float32)[None])
+            elapsed += time.perf_counter() - t0
+            rows += 1
+            blocks += c.n
+            if elapsed >= budget_s:
+                break
+        if elapsed >= budget_s:
+            break
+    threads = 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        pass
+    gbs = blocks * c.slot_bytes / elapsed / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "blocks_per_s": round(blocks / elapsed, 1), "seconds": round(elapsed, 2),
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"project_q + score_blocks + rank_victims of {rows} (layer, sequence) score row(s) "
+                      f"x {c.n} blocks of the same workload, float64 NumPy on the GPU's own q_proj and A_g"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama3_8b_decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the predictor's path has no multi-GPU part here); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rank_kv_block_amd as rk
+    from rank_kv_block_amd.workloads import CONFIGS, Workload
+
+    rk.lib()   # fails loudly when the HIP library is missing
+    c = CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    print(f"[bench] setting up {c.name}: {c.description}", file=sys.stderr, flush=True)
+    wl = Workload(c)
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        wl.step(wl.layer0_for_step(i))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    nl = c.step_layers
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        l0 = wl.layer0_for_step(i)
+        rk.pred_project_kv_block(wl.h, l0, wl.k_new[l0:l0 + nl], wl.table_new[l0:l0 + nl])
+        rk.pred_project_q(wl.h, wl.q[l0:l0 + nl], wl.q_proj)
+        ev[i][0].record(stream)
+        rk.pred_score_blocks(wl.h, l0, wl.q_proj, wl.tables, wl.scores)
+        ev[i][1].record(stream)
+        rk.pred_rank_victims(wl.h, wl.scores.view(nl * c.S, c.n), wl.victims, wl.workspace)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rk.pred_device_error(wl.h)
+
+    step_s = (t1 - t0) / args.steps
+    score_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    blocks = c.blocks_per_step
+    a_g_bytes = blocks * c.slot_bytes
+    aux_bytes = blocks * 8 + nl * c.S * c.M * c.Hq * c.R * 2      # table entry + score per block, q_proj
+    achieved = a_g_bytes / (score_ms * 1e-3) / 1e9
+    out = {
+        "metric": "score_blocks A_g GB/s (% of HBM peak) and blocks scored/s, 1 GPU",
+        "value": round(a_g_bytes / step_s / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; no model weights or datasets)",
+        "config": {"workload": c.name, "description": c.description, "layers_per_step": nl, "sequences": c.S,
+                   "blocks_per_sequence": c.n, "query_rows": c.M, "num_q_heads": c.Hq, "num_kv_heads": c.Hk,
+                   "head_dim": c.D, "r": c.R, "block_size": c.B, "a_g_bytes_per_step": a_g_bytes},
+        "blocks_per_s": round(blocks / step_s, 1),
+        "pct_hbm_peak_step": round(100.0 * a_g_bytes / step_s / 1e9 / HBM_PEAK_GBS, 2),
+        "score_kernel_ms": round(score_ms, 4),
+        "score_kernel_path": "decode_stream" if c.M * c.g <= 16 else "many_row",
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": _traffic(c.name, a_g_bytes),
+            "kernel": "score_decode_kernel",
+            "algorithmic_bytes_per_launch": a_g_bytes,
+            "aux_bytes_per_launch": aux_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    wl.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

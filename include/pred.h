@@ -1,0 +1,202 @@
+/*
+ * pred.h -- C ABI of the low-rank block predictor for a paged KV cache (MI355X / gfx950).
+ *
+ * What it computes (predictor.rs page, module doc): a seeded projection
+ * P [head_dim, r] maps every query (Q @ P) and every key of a KV block (K @ P)
+ * to rank r; the projected keys live in A_g [layers, max_blocks, num_kv_heads,
+ * block_size, r] (bf16, layout comment on a_g_bytes and on the Predictor
+ * fields); a block's score is the max, over query heads, query rows and the
+ * block's tokens, of the projected dot product, and an ascending sort of the
+ * scores ranks eviction victims (lowest score first).
+ *
+ * Conventions for every call below
+ *   - Return value: 0 on success, a negative PRED_ERR_* code on failure; the
+ *     thread-local pred_last_error() string then says what was wrong.  A call
+ *     that fails argument checks enqueues nothing.
+ *   - Pointers marked "device" are HIP device pointers the caller owns and
+ *     keeps alive until the enqueued work has finished; "host" pointers are
+ *     read or written before the call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call except
+ *     pred_create, pred_copy_projection, pred_read_slot and pred_device_error
+ *     only enqueues work on `stream` and returns without synchronising
+ *     (the pages' *_on_stream variants).
+ *   - bf16 tensors are raw IEEE bfloat16 bit patterns (uint16_t), row-major.
+ *   - The library allocates device memory only in pred_create (P, A_g and a
+ *     4-byte error word) and frees it in pred_destroy.
+ */
+#ifndef PRED_H
+#define PRED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t pred_bf16;
+typedef struct pred_handle pred_t;
+
+/* PredictorDims (predictor.rs page).  All fields must be > 0 and
+ * num_q_heads must be a multiple of num_kv_heads (PredictorDims::validate). */
+typedef struct {
+    int32_t num_layers;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t r;
+    int32_t block_size;
+    int64_t max_blocks;
+} pred_dims;
+
+enum {
+    PRED_OK = 0,
+    PRED_ERR_INVALID_DIMS = -1, /* a dim <= 0, nq % nkv != 0, or a size overflows int64 */
+    PRED_ERR_OUT_OF_RANGE = -2, /* layer / block / count outside the dims */
+    PRED_ERR_OOM = -3,          /* A_g does not fit in 95% of free HBM */
+    PRED_ERR_UNSUPPORTED = -4,  /* a shape this library's kernels do not handle */
+    PRED_ERR_NULL_ARG = -5,     /* a required pointer is NULL */
+    PRED_ERR_HIP = -6,          /* a HIP runtime call or kernel launch failed */
+    PRED_ERR_WORKSPACE = -7,    /* workspace missing or too small */
+    PRED_ERR_DEVICE = -8        /* a kernel met an invalid block-table entry */
+};
+
+/* pred_create flags */
+#define PRED_FLAG_ZERO_AG 1u /* zero A_g after allocation (it is left unzeroed by default) */
+
+/* ------------------------------------------------------------------ sizing (pure) */
+
+/* Bytes of A_g: num_layers * max_blocks * num_kv_heads * block_size * r * 2
+ * (predictor.rs page, a_g_bytes).  Returns a negative code if the dims are
+ * invalid or the product overflows. */
+int64_t pred_a_g_bytes(const pred_dims* d);
+
+/* The fit check made by pred_create before it allocates A_g (predictor.rs
+ * page, new_on_stream): A_g must not exceed 95% of `free_bytes`, the rest being
+ * kept for scratch and attention.  Returns 0 if it fits, PRED_ERR_OOM with a
+ * message naming r, max_blocks and the sizing formula otherwise, or
+ * PRED_ERR_INVALID_DIMS.  No device access. */
+int pred_check_fit(const pred_dims* d, uint64_t free_bytes);
+
+/* Largest r and max_blocks this library's kernels accept, and other shape
+ * limits, as a human-readable message (host string, static storage). */
+const char* pred_limits(void);
+
+/* ------------------------------------------------------------------ lifetime */
+
+/* Validate the dims, build P on the host from `seed` (N(0, 1/r) rounded to
+ * bf16 by the SplitMix64 / Box-Muller rule the library documents), check the
+ * fit against hipMemGetInfo, allocate P and A_g on the current device, upload
+ * P on `stream` and synchronise it (predictor.rs page, new_on_stream).
+ * A_g is not zeroed unless PRED_FLAG_ZERO_AG is set: score_blocks may read
+ * slots that project_kv_block never wrote.  On any failure everything
+ * allocated is freed and *out is left NULL. */
+int pred_create(const pred_dims* d, uint64_t seed, uint32_t flags, void* stream, pred_t** out);
+
+/* As pred_create, but P is taken from `p_host` [head_dim, r] bf16 (host) instead
+ * of being generated.  For tests that need a chosen P (identity, hand-worked
+ * examples). */
+int pred_create_with_projection(const pred_dims* d, const pred_bf16* p_host, uint32_t flags,
+                                void* stream, pred_t** out);
+
+/* Free P, A_g and the handle.  Waits for the device first.  NULL is a no-op. */
+void pred_destroy(pred_t* p);
+
+/* ------------------------------------------------------------------ hot path */
+
+/* q_proj = bf16(q @ P) (predictor.rs page, project_q).
+ *   q       device, [n_vec, num_q_heads, head_dim] bf16 (n_vec stacked query rows,
+ *           e.g. layers x sequences x rows)
+ *   q_proj  device, [n_vec, num_q_heads, r] bf16 output
+ * Every output element is the float64 sum of its head_dim exact bf16 products,
+ * rounded once to bf16 (nearest, ties to even).  n_vec == 0 is a no-op. */
+int pred_project_q(pred_t* p, const pred_bf16* q, int64_t n_vec, pred_bf16* q_proj, void* stream);
+
+/* Project whole KV blocks of `n_layers` layers and write their low-rank keys
+ * into A_g through block tables (predictor.rs page, project_kv_block, batched
+ * over blocks and layers).
+ *   k            device, [n_layers, n_blocks, block_size, num_kv_heads, head_dim]
+ *                bf16 (one block per [block_size, num_kv_heads, head_dim] slice,
+ *                the page's k_block layout)
+ *   block_table  device, [n_layers, n_blocks] int32 physical slot ids, or NULL
+ *                for slots 0..n_blocks-1 in every layer
+ * Block i of layer layer0 + l lands in A_g[layer0 + l, block_table[l, i]] as
+ * [num_kv_heads, block_size, r], each element bf16(float64 sum).  Host-side
+ * errors: layers outside [0, num_layers) or (NULL table) n_blocks > max_blocks
+ * -> PRED_ERR_OUT_OF_RANGE.  A table entry outside [0, max_blocks) is skipped on
+ * the device and raises the device error word (see pred_device_error).  Two
+ * entries naming one slot of one layer race.  Any count of zero is a no-op. */
+int pred_project_kv_block(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* k,
+                          const int32_t* block_table, int64_t n_blocks, void* stream);
+
+/* Block scores (predictor.rs page, score_blocks, extended to several layers,
+ * sequences and query rows).
+ *   q_proj        device, [n_layers, n_seqs, n_rows, num_q_heads, r] bf16
+ *   block_tables  device, [n_seqs, n_blocks] int32 physical ids, or NULL for the
+ *                 identity (every sequence reads slots 0..n_blocks-1)
+ *   scores        device, [n_layers, n_seqs, n_blocks] float32 output
+ * scores[l, s, b] = max over rows i, query heads h, tokens t of
+ *   sum_j q_proj[l, s, i, h, j] * A_g[layer0 + l, table[s, b], h / g, t, j]
+ * with g = num_q_heads / num_kv_heads, accumulated in float32, no scale.
+ * Scores are indexed by logical block position b.  Slots never written hold
+ * whatever A_g held.  Errors: layer0 + n_layers > num_layers, n_blocks >
+ * max_blocks with a NULL table -> PRED_ERR_OUT_OF_RANGE.  A table entry outside
+ * [0, max_blocks) gives that block a NaN score and raises the device error word.
+ * Any count of zero is a no-op. */
+int pred_score_blocks(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* q_proj,
+                      int32_t n_rows, const int32_t* block_tables, int64_t n_blocks, int32_t n_seqs,
+                      float* scores, void* stream);
+
+/* Eviction order (predictor.rs page, module doc: scores rank eviction victims;
+ * qsa_select.rs page, host top-k: lower index on ties).
+ *   scores     device, [n_segments, n_blocks] float32
+ *   victims    device, [n_segments, n_blocks] int32 output: each row is the
+ *              permutation of 0..n_blocks-1 that sorts the row's scores
+ *              ascending, equal scores in ascending index order, -0 equal to
+ *              +0, NaN before everything
+ *   workspace  device scratch of at least pred_rank_workspace_bytes() bytes
+ *              (may be NULL when that is 0)
+ * n_blocks must be <= 2^31 - 1. */
+int pred_rank_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments,
+                      int32_t* victims, void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace pred_rank_victims needs for this shape (0 when every segment is
+ * sorted inside one workgroup). */
+size_t pred_rank_workspace_bytes(int64_t n_blocks, int64_t n_segments);
+
+/* ------------------------------------------------------------------ inspection */
+
+/* The P that pred_create builds for (head_dim, r, seed), computed on the host
+ * only (no device needed): `out` is [head_dim, r] bf16.  Returns
+ * PRED_ERR_INVALID_DIMS for non-positive sizes. */
+int pred_projection_host(int32_t head_dim, int32_t r, uint64_t seed, pred_bf16* out);
+
+/* Copy P [head_dim, r] bf16 to `host_out` (synchronous). */
+int pred_copy_projection(pred_t* p, pred_bf16* host_out);
+
+/* Device address of A_g [num_layers, max_blocks, num_kv_heads, block_size, r]
+ * bf16 (predictor.rs page, a_g_dev_ptr).  The library owns it. */
+void* pred_a_g_ptr(pred_t* p);
+
+/* Copy the A_g slot (layer, block) [num_kv_heads, block_size, r] bf16 to
+ * `host_out` and synchronise `stream` (predictor.rs page, read_k_lr_slot). */
+int pred_read_slot(pred_t* p, int32_t layer, int64_t block, pred_bf16* host_out, void* stream);
+
+/* The dims the handle was created with (predictor.rs page, dims). */
+int pred_get_dims(pred_t* p, pred_dims* out);
+
+/* Synchronise `stream`, read and clear the device error word.  Returns 0, or
+ * PRED_ERR_DEVICE if a kernel since the last call met an invalid table entry. */
+int pred_device_error(pred_t* p, void* stream);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* pred_last_error(void);
+
+/* Library version string. */
+const char* pred_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRED_H */

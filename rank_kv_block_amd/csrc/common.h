@@ -1,0 +1,74 @@
+// Shared device/host helpers of the predictor library (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+namespace pred {
+
+// Bits of the device error word.
+enum : uint32_t { DEVERR_TABLE = 1u };
+
+__host__ __device__ inline uint64_t f64_bits(double x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return (uint64_t)__double_as_longlong(x);
+#else
+    uint64_t b;
+    memcpy(&b, &x, 8);
+    return b;
+#endif
+}
+
+// float64 -> bf16 bit pattern, round to nearest, ties to even, in one step from
+// the float64 value (no float32 intermediate, so no double rounding).  Keeps
+// bf16 subnormals, overflows to +/-inf, maps NaN to 0x7FC0.
+//
+// Works on the integer significand: the bf16 quantum is 2^qe with
+// qe = max(e, -126) - 7 for a value with leading-bit exponent e; the
+// significand is shifted right to units of 2^qe and rounded half-even on the
+// bits shifted out.  The biased bf16 pattern is then ((qe + 133) << 7) + n,
+// which also carries a rounding overflow of n = 256 into the exponent and gives
+// the subnormal encoding when qe = -133.
+__host__ __device__ inline uint16_t f64_to_bf16_rne(double x) {
+    const uint64_t b = f64_bits(x);
+    const uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
+    const uint64_t a = b & 0x7FFFFFFFFFFFFFFFull;
+    if (a > 0x7FF0000000000000ull) return 0x7FC0;     // NaN
+    const int biased = (int)(a >> 52);
+    if (biased == 0) return (uint16_t)sign;            // zero / float64 subnormal -> +/-0
+    const int e = biased - 1023;
+    if (e >= 128) return (uint16_t)(sign | 0x7F80u);   // >= 2^128, inf
+    const uint64_t sig = (a & 0x000FFFFFFFFFFFFFull) | 0x0010000000000000ull;
+    const int qe = (e > -126 ? e : -126) - 7;
+    const int s = 52 + qe - e;                         // >= 45
+    uint64_t n = 0;
+    if (s < 64) {
+        n = sig >> s;
+        const uint64_t rem = sig & ((1ull << s) - 1ull);
+        const uint64_t half = 1ull << (s - 1);
+        if (rem > half || (rem == half && (n & 1ull))) ++n;
+    }
+    uint32_t mag = ((uint32_t)(qe + 133) << 7) + (uint32_t)n;
+    if (mag >= 0x7F80u) mag = 0x7F80u;
+    return (uint16_t)(sign | mag);
+}
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Totally ordered uint32 key of a float32 score: ascending key = ascending
+// score; -0 and +0 share a key; every NaN gets key 0 (ranks first).
+__device__ inline uint32_t order_key(float x) {
+    uint32_t u = __float_as_uint(x);
+    if (u == 0x80000000u) u = 0u;
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;
+    return (u & 0x80000000u) ? ~u : (u ^ 0x80000000u);
+}
+
+__device__ inline float key_to_float(uint32_t k) {
+    if (k == 0u) return __uint_as_float(0x7FC00000u);
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+}  // namespace pred

@@ -1,0 +1,366 @@
+// C ABI of the block predictor: argument checks, ownership of P and A_g, and
+// dispatch to the HIP kernels.  The call shapes follow the predictor.rs page
+// (Predictor::new_on_stream, project_q, project_kv_block, score_blocks,
+// a_g_dev_ptr, dims, read_k_lr_slot), batched over blocks, layers, sequences
+// and query rows, plus the victim ranking the page's module doc describes.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+#include "pred.h"
+
+namespace pred {
+void build_projection(int head_dim, int r, uint64_t seed, uint16_t* out);
+hipError_t launch_score_prefill(const ScoreArgs& a, hipStream_t stream);
+bool prefill_supported(const ScoreArgs& a);
+}  // namespace pred
+
+struct pred_handle {
+    pred_dims d;
+    int device;
+    uint16_t* p_dev;   // [D, R] bf16
+    double* pf_dev;    // [D, R] float64 copy read by the projection kernels
+    uint16_t* ag_dev;  // [L, N, Hk, B, R] bf16
+    uint32_t* err_dev; // device error word
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[2048];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return PRED_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(PRED_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+// Dims check of PredictorDims::validate (nq a multiple of nkv) plus positivity
+// and overflow of A_g's size.  Returns the A_g byte count or a negative code.
+int64_t checked_a_g_bytes(const pred_dims* d) {
+    if (!d) return fail(PRED_ERR_NULL_ARG, "dims is NULL");
+    if (d->num_layers <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 || d->r <= 0 ||
+        d->block_size <= 0 || d->max_blocks <= 0)
+        return fail(PRED_ERR_INVALID_DIMS,
+                    "every dim must be > 0 (layers %d, q heads %d, kv heads %d, head_dim %d, r %d, block_size %d, "
+                    "max_blocks %lld)",
+                    d->num_layers, d->num_q_heads, d->num_kv_heads, d->head_dim, d->r, d->block_size,
+                    (long long)d->max_blocks);
+    if (d->num_q_heads % d->num_kv_heads != 0)
+        return fail(PRED_ERR_INVALID_DIMS, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                    d->num_q_heads, d->num_kv_heads);
+    int64_t v = d->num_layers;
+    if (!mul_ok(v, d->max_blocks, &v) || !mul_ok(v, d->num_kv_heads, &v) || !mul_ok(v, d->block_size, &v) ||
+        !mul_ok(v, d->r, &v) || !mul_ok(v, 2, &v))
+        return fail(PRED_ERR_INVALID_DIMS, "A_g size overflows 64 bits");
+    return v;
+}
+
+int check_supported(const pred_dims* d) {
+    if (d->head_dim % 8 != 0 || d->r % 8 != 0)
+        return fail(PRED_ERR_UNSUPPORTED, "head_dim (%d) and r (%d) must be multiples of 8 (16-byte vectors)",
+                    d->head_dim, d->r);
+    if (d->r > 256) return fail(PRED_ERR_UNSUPPORTED, "r (%d) above 256", d->r);
+    if (d->head_dim > 65536) return fail(PRED_ERR_UNSUPPORTED, "head_dim (%d) above 65536", d->head_dim);
+    return PRED_OK;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+int create_impl(const pred_dims* d, const uint16_t* p_host_in, uint64_t seed, uint32_t flags, void* stream,
+                pred_t** out) {
+    if (!out) return fail(PRED_ERR_NULL_ARG, "out is NULL");
+    *out = nullptr;
+    const int64_t need = checked_a_g_bytes(d);
+    if (need < 0) return (int)need;
+    int rc = check_supported(d);
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+
+    const int64_t pn = (int64_t)d->head_dim * d->r;
+    std::vector<uint16_t> p_host((size_t)pn);
+    if (p_host_in) memcpy(p_host.data(), p_host_in, (size_t)pn * 2);
+    else pred::build_projection(d->head_dim, d->r, seed, p_host.data());
+    std::vector<double> pf_host((size_t)pn);
+    for (int64_t i = 0; i < pn; ++i) {
+        uint32_t w = (uint32_t)p_host[i] << 16;
+        float f;
+        memcpy(&f, &w, 4);
+        pf_host[i] = (double)f;
+    }
+
+    size_t free_b = 0, total_b = 0;
+    hipError_t e = hipMemGetInfo(&free_b, &total_b);
+    if (e != hipSuccess) return hip_fail(e, "hipMemGetInfo");
+    rc = pred_check_fit(d, (uint64_t)free_b);
+    if (rc) return rc;
+
+    pred_t* p = new pred_t();
+    p->d = *d;
+    hipGetDevice(&p->device);
+    auto cleanup = [&](int code) {
+        if (p->p_dev) hipFree(p->p_dev);
+        if (p->pf_dev) hipFree(p->pf_dev);
+        if (p->ag_dev) hipFree(p->ag_dev);
+        if (p->err_dev) hipFree(p->err_dev);
+        delete p;
+        return code;
+    };
+    if ((e = hipMalloc(&p->p_dev, (size_t)pn * 2)) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(P)"));
+    if ((e = hipMalloc(&p->pf_dev, (size_t)pn * 8)) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(P f64)"));
+    if ((e = hipMalloc(&p->err_dev, 4)) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(error word)"));
+    if ((e = hipMalloc(&p->ag_dev, (size_t)need)) != hipSuccess)
+        return cleanup(fail(PRED_ERR_OOM, "hipMalloc of A_g (%lld bytes) failed: %s", (long long)need,
+                            hipGetErrorString(e)));
+    if ((e = hipMemcpyAsync(p->p_dev, p_host.data(), (size_t)pn * 2, hipMemcpyHostToDevice, st)) != hipSuccess)
+        return cleanup(hip_fail(e, "upload P"));
+    if ((e = hipMemcpyAsync(p->pf_dev, pf_host.data(), (size_t)pn * 8, hipMemcpyHostToDevice, st)) != hipSuccess)
+        return cleanup(hip_fail(e, "upload P f64"));
+    if ((e = hipMemsetAsync(p->err_dev, 0, 4, st)) != hipSuccess) return cleanup(hip_fail(e, "clear error word"));
+    if (flags & PRED_FLAG_ZERO_AG) {
+        if ((e = hipMemsetAsync(p->ag_dev, 0, (size_t)need, st)) != hipSuccess)
+            return cleanup(hip_fail(e, "zero A_g"));
+    }
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return cleanup(hip_fail(e, "hipStreamSynchronize"));
+    *out = p;
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t pred_a_g_bytes(const pred_dims* d) {
+    const int64_t v = checked_a_g_bytes(d);
+    if (v >= 0) ok();
+    return v;
+}
+
+int pred_check_fit(const pred_dims* d, uint64_t free_bytes) {
+    const int64_t need = checked_a_g_bytes(d);
+    if (need < 0) return (int)need;
+    // 5% of free memory stays for scratch and attention buffers.
+    const uint64_t budget = (free_bytes / 100u) * 95u + (free_bytes % 100u) * 95u / 100u;
+    if ((uint64_t)need > budget) {
+        return fail(PRED_ERR_OOM,
+                    "predictor A_g would need %.2f GiB but only %.2f GiB fits in 95%% of the %.2f GiB of free HBM "
+                    "(5%% is kept for scratch and attention). Shrink one of: r = %d (r = %d halves A_g); "
+                    "max_blocks = %lld (halving the maximum sequence length halves A_g); the KV-cache footprint or "
+                    "other allocations, to free HBM. A_g bytes = num_layers (%d) x max_blocks (%lld) x "
+                    "num_kv_heads (%d) x block_size (%d) x r (%d) x 2.",
+                    need / 1073741824.0, budget / 1073741824.0, free_bytes / 1073741824.0, d->r, d->r / 2,
+                    (long long)d->max_blocks, d->num_layers, (long long)d->max_blocks, d->num_kv_heads,
+                    d->block_size, d->r);
+    }
+    return ok();
+}
+
+const char* pred_limits(void) {
+    return "head_dim and r multiples of 8; r <= 256; head_dim <= 65536; 16-byte aligned q, q_proj and k "
+           "buffers. Streaming decode scorer: r in {16,32,64,128} and block_size*r/8 a power of two <= 1024; "
+           "other shapes use a plain per-block kernel. Rank: n_blocks <= 2^31-1 (above 16384 per segment a "
+           "workspace of 16*n_blocks*n_segments bytes is needed).";
+}
+
+const char* pred_version(void) { return "rank_kv_block_amd 0.1 (gfx950)"; }
+
+int pred_create(const pred_dims* d, uint64_t seed, uint32_t flags, void* stream, pred_t** out) {
+    return create_impl(d, nullptr, seed, flags, stream, out);
+}
+
+int pred_create_with_projection(const pred_dims* d, const pred_bf16* p_host, uint32_t flags, void* stream,
+                                pred_t** out) {
+    if (!p_host) return fail(PRED_ERR_NULL_ARG, "p_host is NULL");
+    return create_impl(d, p_host, 0, flags, stream, out);
+}
+
+void pred_destroy(pred_t* p) {
+    if (!p) return;
+    int cur = 0;
+    hipGetDevice(&cur);
+    hipSetDevice(p->device);
+    hipDeviceSynchronize();
+    hipFree(p->p_dev);
+    hipFree(p->pf_dev);
+    hipFree(p->ag_dev);
+    hipFree(p->err_dev);
+    hipSetDevice(cur);
+    delete p;
+}
+
+int pred_project_q(pred_t* p, const pred_bf16* q, int64_t n_vec, pred_bf16* q_proj, void* stream) {
+    if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
+    if (n_vec < 0) return fail(PRED_ERR_OUT_OF_RANGE, "n_vec (%lld) < 0", (long long)n_vec);
+    if (n_vec == 0) return ok();
+    if (!q || !q_proj) return fail(PRED_ERR_NULL_ARG, "q or q_proj is NULL");
+    if (!aligned16(q) || !aligned16(q_proj)) return fail(PRED_ERR_UNSUPPORTED, "q and q_proj must be 16-byte aligned");
+    int64_t rows;
+    if (!mul_ok(n_vec, p->d.num_q_heads, &rows)) return fail(PRED_ERR_OUT_OF_RANGE, "n_vec too large");
+    hipError_t e = pred::launch_project_dense(q, p->pf_dev, q_proj, rows, p->d.head_dim, p->d.r, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "project_q launch");
+    return ok();
+}
+
+int pred_project_kv_block(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* k,
+                          const int32_t* block_table, int64_t n_blocks, void* stream) {
+    if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
+    if (layer0 < 0 || n_layers < 0 || (int64_t)layer0 + n_layers > p->d.num_layers)
+        return fail(PRED_ERR_OUT_OF_RANGE, "project_kv_block out of range: layers [%d, %d) of %d", layer0,
+                    layer0 + n_layers, p->d.num_layers);
+    if (n_blocks < 0) return fail(PRED_ERR_OUT_OF_RANGE, "n_blocks (%lld) < 0", (long long)n_blocks);
+    if (!block_table && n_blocks > p->d.max_blocks)
+        return fail(PRED_ERR_OUT_OF_RANGE, "project_kv_block out of range: %lld blocks without a table, max_blocks %lld",
+                    (long long)n_blocks, (long long)p->d.max_blocks);
+    if (n_blocks == 0 || n_layers == 0) return ok();
+    if (!k) return fail(PRED_ERR_NULL_ARG, "k is NULL");
+    if (!aligned16(k)) return fail(PRED_ERR_UNSUPPORTED, "k must be 16-byte aligned");
+    const pred_dims& d = p->d;
+    uint16_t* a_first = p->ag_dev + (int64_t)layer0 * d.max_blocks * d.num_kv_heads * d.block_size * d.r;
+    hipError_t e = pred::launch_project_paged(k, p->pf_dev, a_first, block_table, n_layers, n_blocks, d.max_blocks,
+                                              d.num_kv_heads, d.block_size, d.head_dim, d.r, p->err_dev,
+                                              (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "project_kv_block launch");
+    return ok();
+}
+
+int pred_score_blocks(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* q_proj, int32_t n_rows,
+                      const int32_t* block_tables, int64_t n_blocks, int32_t n_seqs, float* scores, void* stream) {
+    if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
+    if (layer0 < 0 || n_layers < 0 || (int64_t)layer0 + n_layers > p->d.num_layers)
+        return fail(PRED_ERR_OUT_OF_RANGE, "score_blocks layers [%d, %d) outside [0, %d)", layer0, layer0 + n_layers,
+                    p->d.num_layers);
+    if (n_blocks < 0 || n_seqs < 0 || n_rows < 0)
+        return fail(PRED_ERR_OUT_OF_RANGE, "negative count (n_blocks %lld, n_seqs %d, n_rows %d)",
+                    (long long)n_blocks, n_seqs, n_rows);
+    if (!block_tables && n_blocks > p->d.max_blocks)
+        return fail(PRED_ERR_OUT_OF_RANGE, "score_blocks: %lld blocks without a table, max_blocks %lld",
+                    (long long)n_blocks, (long long)p->d.max_blocks);
+    if (n_layers == 0 || n_blocks == 0 || n_seqs == 0) return ok();
+    if (n_rows == 0) return fail(PRED_ERR_OUT_OF_RANGE, "n_rows must be >= 1");
+    if (!q_proj || !scores) return fail(PRED_ERR_NULL_ARG, "q_proj or scores is NULL");
+    if (!aligned16(q_proj)) return fail(PRED_ERR_UNSUPPORTED, "q_proj must be 16-byte aligned");
+    pred::ScoreArgs a;
+    a.qp = q_proj;
+    a.ag = p->ag_dev;
+    a.tables = block_tables;
+    a.scores = scores;
+    a.err = p->err_dev;
+    a.N = p->d.max_blocks;
+    a.n = n_blocks;
+    a.layer0 = layer0;
+    a.n_layers = n_layers;
+    a.S = n_seqs;
+    a.M = n_rows;
+    a.Hq = p->d.num_q_heads;
+    a.Hk = p->d.num_kv_heads;
+    a.B = p->d.block_size;
+    a.R = p->d.r;
+    hipError_t e;
+    const int g = a.Hq / a.Hk;
+    if ((int64_t)a.M * g > 16 && pred::prefill_supported(a)) e = pred::launch_score_prefill(a, (hipStream_t)stream);
+    else e = pred::launch_score_decode_or_generic(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "score_blocks launch");
+    return ok();
+}
+
+int pred_rank_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments, int32_t* victims,
+                      void* workspace, size_t ws_bytes, void* stream) {
+    if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
+    if (n_blocks < 0 || n_segments < 0)
+        return fail(PRED_ERR_OUT_OF_RANGE, "negative count (n_blocks %lld, n_segments %lld)", (long long)n_blocks,
+                    (long long)n_segments);
+    if (n_blocks > 2147483647LL) return fail(PRED_ERR_OUT_OF_RANGE, "n_blocks above 2^31-1");
+    if (n_blocks == 0 || n_segments == 0) return ok();
+    if (!scores || !victims) return fail(PRED_ERR_NULL_ARG, "scores or victims is NULL");
+    const size_t need = pred::rank_workspace_bytes(n_blocks, n_segments);
+    if (need > 0 && (!workspace || ws_bytes < need))
+        return fail(PRED_ERR_WORKSPACE, "rank_victims needs a %zu-byte workspace (%zu given)", need,
+                    workspace ? ws_bytes : (size_t)0);
+    if (need > 0 && ((uintptr_t)workspace & 7u)) return fail(PRED_ERR_WORKSPACE, "workspace must be 8-byte aligned");
+    hipError_t e = pred::launch_rank(scores, n_blocks, n_segments, victims, workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "rank_victims launch");
+    return ok();
+}
+
+size_t pred_rank_workspace_bytes(int64_t n_blocks, int64_t n_segments) {
+    return pred::rank_workspace_bytes(n_blocks, n_segments);
+}
+
+int pred_projection_host(int32_t head_dim, int32_t r, uint64_t seed, pred_bf16* out) {
+    if (!out) return fail(PRED_ERR_NULL_ARG, "out is NULL");
+    if (head_dim <= 0 || r <= 0) return fail(PRED_ERR_INVALID_DIMS, "head_dim and r must be > 0");
+    pred::build_projection(head_dim, r, seed, out);
+    return ok();
+}
+
+int pred_copy_projection(pred_t* p, pred_bf16* host_out) {
+    if (!p || !host_out) return fail(PRED_ERR_NULL_ARG, "predictor or host_out is NULL");
+    hipError_t e = hipMemcpy(host_out, p->p_dev, (size_t)p->d.head_dim * p->d.r * 2, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "copy P");
+    return ok();
+}
+
+void* pred_a_g_ptr(pred_t* p) { return p ? p->ag_dev : nullptr; }
+
+int pred_read_slot(pred_t* p, int32_t layer, int64_t block, pred_bf16* host_out, void* stream) {
+    if (!p || !host_out) return fail(PRED_ERR_NULL_ARG, "predictor or host_out is NULL");
+    if (layer < 0 || layer >= p->d.num_layers || block < 0 || block >= p->d.max_blocks)
+        return fail(PRED_ERR_OUT_OF_RANGE, "read_slot out of range: layer %d, block %lld", layer, (long long)block);
+    const pred_dims& d = p->d;
+    const int64_t slot = (int64_t)d.num_kv_heads * d.block_size * d.r;
+    const uint16_t* src = p->ag_dev + ((int64_t)layer * d.max_blocks + block) * slot;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(host_out, src, (size_t)slot * 2, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "read slot");
+    return ok();
+}
+
+int pred_get_dims(pred_t* p, pred_dims* out) {
+    if (!p || !out) return fail(PRED_ERR_NULL_ARG, "predictor or out is NULL");
+    *out = p->d;
+    return ok();
+}
+
+int pred_device_error(pred_t* p, void* stream) {
+    if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    uint32_t w = 0;
+    e = hipMemcpy(&w, p->err_dev, 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "read error word");
+    if (w) {
+        e = hipMemset(p->err_dev, 0, 4);
+        if (e != hipSuccess) return hip_fail(e, "clear error word");
+        return fail(PRED_ERR_DEVICE, "a kernel met a block-table entry outside [0, max_blocks) (flags 0x%x)", w);
+    }
+    return ok();
+}
+
+const char* pred_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,343 @@
+// Decode block scorer (predictor.rs page: score_blocks / predictor_score):
+//   score[l, s, b] = max over rows i, heads h, tokens t of
+//                    sum_j q_proj[l, s, i, h, j] * A_g[layer0 + l, table[s, b], h / g, t, j]
+// for the case where a kv head's query set (rows x GQA group, padded to a power
+// of two QH <= 16) fits in registers.  The kernel streams A_g once.
+//
+// Data layout per A_g slot: [Hk][B][R] bf16.  A kv head's region of one slot is
+// B rows of R values, U = B * R / 8 chunks of 16 bytes.  A wave reads 64
+// consecutive chunks with one 16-byte load per lane (1 KiB, fully coalesced);
+// LPR = R / 8 consecutive lanes hold one row, lane p of a row holding values
+// [8p, 8p + 8).  A lane takes the dot products of its 8 values with all QH
+// queries of the kv head (4 v_dot2c_f32_bf16 each) and the LPR lanes of a row
+// then add their partial sums with DPP.
+//
+// Reduction across a row without a full butterfly per head: lane p keeps its
+// partial sums in a lane-specific order -- register i holds head label
+// i ^ f(p).  At level m the partner lane is p ^ M_m (M = 1, 2, 7, 15, 16:
+// quad_perm, quad_perm, row_half_mirror, row_mirror, swizzle), each lane keeps
+// the lower half of its registers and adds the partner's upper half.  With
+// f linear over GF(2) and f(M_m) = QH >> (m + 1) the labels the two lanes add
+// are the same head, so level m costs QH >> (m + 1) DPP adds instead of QH,
+// and after log2(LPR) levels each lane holds complete dot products of
+// max(QH / LPR, 1) heads.  The block max then needs no sums at all.
+#include "common.h"
+#include "kernels.h"
+
+namespace pred {
+
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                          false);
+}
+
+// Value of `v` held by this lane's partner at reduction level M.
+template <int M>
+__device__ inline float partner(float v) {
+    if constexpr (M == 0) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));  // xor 1
+    } else if constexpr (M == 1) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));  // xor 2
+    } else if constexpr (M == 2) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));  // 7 - p
+    } else if constexpr (M == 3) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true));  // 15 - p
+    } else {
+        return __shfl_xor(v, 16);  // xor 16
+    }
+}
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
+
+// Label offset f(p): decompose p over the level masks (1, 2, 7, 15, 16), whose
+// top bits are bits 0..4, and xor together the QH >> (m + 1) of the masks used.
+template <int LPR, int QH>
+__device__ inline int label_xor(int p) {
+    constexpr int msk[5] = {1, 2, 7, 15, 16};
+    int f = 0;
+#pragma unroll
+    for (int m = ilog2(LPR) - 1; m >= 0; --m) {
+        if ((p >> m) & 1) {
+            p ^= msk[m];
+            f ^= (QH >> (m + 1));
+        }
+    }
+    return f;
+}
+
+template <int LPR, int QH, int M>
+__device__ inline void reduce_levels(float* v) {
+    if constexpr ((1 << M) < LPR) {
+        constexpr int w = (QH >> M) > 0 ? (QH >> M) : 1;
+        if constexpr (w >= 2) {
+#pragma unroll
+            for (int i = 0; i < w / 2; ++i) v[i] += partner<M>(v[i + w / 2]);
+        } else {
+            v[0] += partner<M>(v[0]);
+        }
+        reduce_levels<LPR, QH, M + 1>(v);
+    }
+}
+
+__device__ inline float wave_max_xor(float v, int upto) {
+    // max over aligned groups of `upto` lanes (power of two, <= 64)
+    if (upto > 1) v = fmaxf(v, partner<0>(v));
+    if (upto > 2) v = fmaxf(v, partner<1>(v));
+    if (upto > 4) v = fmaxf(v, partner<2>(v));
+    if (upto > 8) v = fmaxf(v, partner<3>(v));
+    if (upto > 16) v = fmaxf(v, __shfl_xor(v, 16));
+    if (upto > 32) v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+struct DecodeGeom {
+    int U, log2U;          // chunks per (block, kv head) region; U is a power of two
+    int NBW;               // blocks per wave
+    int SPB;               // load slots per block (U / 64 when U >= 64, else 1)
+    int n_eff;             // effective heads per kv head = M * g
+    int n_groups;          // ceil(n_eff / QH)
+    int64_t waves_per_seq;
+    int64_t total_waves;
+};
+
+template <int LPR, int QH, int NS>
+__global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wave >= gm.total_waves) return;
+    const int64_t wb = wave % gm.waves_per_seq;
+    const int64_t ls = wave / gm.waves_per_seq;
+    const int s = (int)(ls % a.S);
+    const int l = (int)(ls / a.S);
+    const int64_t b_first = wb * gm.NBW;
+    const int p = lane & (LPR - 1);
+    const int g = a.Hq / a.Hk;
+    const int64_t layer = a.layer0 + l;
+    const int64_t slot_elems = (int64_t)a.Hk * a.B * a.R;
+
+    // Per load slot: the lane's row of its block's region (kv head 0).  Slots
+    // past the end or with an invalid table entry read A_g's first row instead
+    // (always mapped) and are masked out of the max, so the loads need no branch.
+    const uint16_t* base[NS];
+    uint32_t live = 0;
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+        const int f = sl * 64 + lane;
+        const int bi = f >> gm.log2U;
+        const int t = (f & (gm.U - 1)) / LPR;
+        const int64_t b = b_first + bi;
+        base[sl] = a.ag + p * 8;
+        if (bi < gm.NBW && b < a.n) {
+            const int64_t phys = a.tables ? (int64_t)a.tables[(int64_t)s * a.n + b] : b;
+            if (phys >= 0 && phys < a.N) {
+                base[sl] = a.ag + (layer * a.N + phys) * slot_elems + (int64_t)t * a.R + p * 8;
+                live |= 1u << sl;
+            }
+        }
+    }
+
+    float rm[NS];
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) rm[sl] = -__builtin_inff();
+
+    const uint16_t* qrows = a.qp + ((int64_t)l * a.S + s) * (int64_t)a.M * a.Hq * a.R;
+    const int fx = label_xor<LPR, QH>(p);
+    const int64_t kv_stride = (int64_t)a.B * a.R;
+
+    for (int hg = 0; hg < gm.n_groups; ++hg) {
+        for (int kv = 0; kv < a.Hk; ++kv) {
+            uint32_t q[QH][4];
+#pragma unroll
+            for (int i = 0; i < QH; ++i) {
+                int e = hg * QH + (i ^ fx);
+                if (e >= gm.n_eff) e = gm.n_eff - 1;  // padding: repeat a real head (max unchanged)
+                const int row = e / g;
+                const int h = e - row * g;
+                const uint4 w = *reinterpret_cast<const uint4*>(
+                    qrows + ((int64_t)row * a.Hq + kv * g + h) * a.R + p * 8);
+                q[i][0] = w.x; q[i][1] = w.y; q[i][2] = w.z; q[i][3] = w.w;
+            }
+            uint4 av[NS];
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl)
+                av[sl] = *reinterpret_cast<const uint4*>(base[sl] + ((live >> sl) & 1u ? kv * kv_stride : 0));
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl) {
+                float v[QH];
+#pragma unroll
+                for (int i = 0; i < QH; ++i) {
+                    float acc = dot2(av[sl].x, q[i][0], 0.0f);
+                    acc = dot2(av[sl].y, q[i][1], acc);
+                    acc = dot2(av[sl].z, q[i][2], acc);
+                    v[i] = dot2(av[sl].w, q[i][3], acc);
+                }
+                reduce_levels<LPR, QH, 0>(v);
+                constexpr int rem = (QH / LPR) > 0 ? (QH / LPR) : 1;
+                float mx = v[0];
+#pragma unroll
+                for (int i = 1; i < rem; ++i) mx = fmaxf(mx, v[i]);
+                rm[sl] = ((live >> sl) & 1u) ? fmaxf(rm[sl], mx) : rm[sl];
+            }
+        }
+    }
+
+    // Block maxima and stores.
+    float* out = a.scores + ((int64_t)l * a.S + s) * a.n;
+    if (gm.U >= 64) {
+        float acc = -__builtin_inff();
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+            acc = fmaxf(acc, rm[sl]);
+            if ((sl + 1) % gm.SPB == 0) {
+                const float v = wave_max_xor(acc, 64);
+                const int bi = sl / gm.SPB;
+                const int64_t b = b_first + bi;
+                if (lane == 0 && bi < gm.NBW && b < a.n) {
+                    const int64_t phys = a.tables ? (int64_t)a.tables[(int64_t)s * a.n + b] : b;
+                    if (phys >= 0 && phys < a.N) {
+                        out[b] = v;
+                    } else {
+                        out[b] = __uint_as_float(0x7FC00000u);
+                        atomicOr(a.err, DEVERR_TABLE);
+                    }
+                }
+                acc = -__builtin_inff();
+            }
+        }
+    } else {
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+            const float v = wave_max_xor(rm[sl], gm.U);
+            const int f = sl * 64 + lane;
+            const int bi = f >> gm.log2U;
+            const int64_t b = b_first + bi;
+            if ((lane & (gm.U - 1)) == 0 && bi < gm.NBW && b < a.n) {
+                const int64_t phys = a.tables ? (int64_t)a.tables[(int64_t)s * a.n + b] : b;
+                if (phys >= 0 && phys < a.N) {
+                    out[b] = v;
+                } else {
+                    out[b] = __uint_as_float(0x7FC00000u);
+                    atomicOr(a.err, DEVERR_TABLE);
+                }
+            }
+        }
+    }
+}
+
+// Any shape: one thread per (layer, sequence, block), plain loops.  Used when
+// R or block_size is not one the streaming kernel is laid out for.
+__global__ __launch_bounds__(256) void score_generic_kernel(ScoreArgs a) {
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)a.n_layers * a.S * a.n;
+    if (id >= total) return;
+    const int64_t b = id % a.n;
+    const int64_t ls = id / a.n;
+    const int s = (int)(ls % a.S);
+    const int l = (int)(ls / a.S);
+    const int g = a.Hq / a.Hk;
+    const int64_t phys = a.tables ? (int64_t)a.tables[(int64_t)s * a.n + b] : b;
+    if (phys < 0 || phys >= a.N) {
+        a.scores[id] = __uint_as_float(0x7FC00000u);
+        atomicOr(a.err, DEVERR_TABLE);
+        return;
+    }
+    const uint16_t* slot = a.ag + ((a.layer0 + l) * a.N + phys) * (int64_t)a.Hk * a.B * a.R;
+    const uint16_t* qrows = a.qp + ((int64_t)l * a.S + s) * (int64_t)a.M * a.Hq * a.R;
+    float best = -__builtin_inff();
+    for (int i = 0; i < a.M; ++i)
+        for (int h = 0; h < a.Hq; ++h) {
+            const uint16_t* qv = qrows + ((int64_t)i * a.Hq + h) * a.R;
+            const uint16_t* kbase = slot + (int64_t)(h / g) * a.B * a.R;
+            for (int t = 0; t < a.B; ++t) {
+                float acc = 0.0f;
+                for (int j = 0; j < a.R; ++j)
+                    acc = __builtin_fmaf(__uint_as_float((uint32_t)qv[j] << 16),
+                                         __uint_as_float((uint32_t)kbase[(int64_t)t * a.R + j] << 16), acc);
+                best = fmaxf(best, acc);
+            }
+        }
+    a.scores[id] = best;
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int pick_qh(int n_eff) {
+    int qh = 1;
+    while (qh < n_eff && qh < 16) qh <<= 1;
+    return qh;
+}
+
+template <int LPR, int QH, int NS>
+void launch_decode_t(const ScoreArgs& a, const DecodeGeom& gm, hipStream_t st) {
+    const unsigned grid = (unsigned)((gm.total_waves + 3) / 4);
+    score_decode_kernel<LPR, QH, NS><<<grid, 256, 0, st>>>(a, gm);
+}
+
+template <int LPR, int NS>
+void launch_decode_qh(const ScoreArgs& a, const DecodeGeom& gm, int qh, hipStream_t st) {
+    switch (qh) {
+        case 1: launch_decode_t<LPR, 1, NS>(a, gm, st); break;
+        case 2: launch_decode_t<LPR, 2, NS>(a, gm, st); break;
+        case 4: launch_decode_t<LPR, 4, NS>(a, gm, st); break;
+        case 8: launch_decode_t<LPR, 8, NS>(a, gm, st); break;
+        default: launch_decode_t<LPR, 16, NS>(a, gm, st); break;
+    }
+}
+
+template <int NS>
+void launch_decode_ns(const ScoreArgs& a, const DecodeGeom& gm, int lpr, int qh, hipStream_t st) {
+    switch (lpr) {
+        case 2: launch_decode_qh<2, NS>(a, gm, qh, st); break;
+        case 4: launch_decode_qh<4, NS>(a, gm, qh, st); break;
+        case 8: launch_decode_qh<8, NS>(a, gm, qh, st); break;
+        default: launch_decode_qh<16, NS>(a, gm, qh, st); break;
+    }
+}
+
+bool decode_geometry(const ScoreArgs& a, DecodeGeom& gm, int& ns, int& lpr, int& qh) {
+    if (!(a.R == 16 || a.R == 32 || a.R == 64 || a.R == 128)) return false;
+    lpr = a.R / 8;
+    const int64_t U = (int64_t)a.B * lpr;
+    if (!is_pow2(U) || U > 1024) return false;
+    gm.U = (int)U;
+    gm.log2U = 0;
+    while ((1 << gm.log2U) < gm.U) ++gm.log2U;
+    ns = (U >= 512) ? 16 : 8;
+    const int chunks = ns * 64;
+    gm.NBW = (int)(chunks / U);
+    gm.SPB = U >= 64 ? (int)(U / 64) : 1;
+    const int g = a.Hq / a.Hk;
+    gm.n_eff = a.M * g;
+    qh = pick_qh(gm.n_eff);
+    gm.n_groups = (gm.n_eff + qh - 1) / qh;
+    gm.waves_per_seq = (a.n + gm.NBW - 1) / gm.NBW;
+    gm.total_waves = gm.waves_per_seq * a.S * a.n_layers;
+    return true;
+}
+
+}  // namespace
+
+hipError_t launch_score_decode_or_generic(const ScoreArgs& a, hipStream_t stream) {
+    DecodeGeom gm;
+    int ns, lpr, qh;
+    if (decode_geometry(a, gm, ns, lpr, qh)) {
+        if (ns == 16) launch_decode_ns<16>(a, gm, lpr, qh, stream);
+        else launch_decode_ns<8>(a, gm, lpr, qh, stream);
+    } else {
+        const int64_t total = (int64_t)a.n_layers * a.S * a.n;
+        score_generic_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(a);
+    }
+    return hipGetLastError();
+}
+
+const char* score_decode_path_name(const ScoreArgs& a) {
+    DecodeGeom gm;
+    int ns, lpr, qh;
+    return decode_geometry(a, gm, ns, lpr, qh) ? "decode_stream" : "generic";
+}
+
+}  // namespace pred

@@ -1,0 +1,124 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and its
+pure functions and argument checks behave as include/pred.h states (no device needed)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import rank_kv_block_amd as rk
+from oracle import prng
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pred.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pred_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = rk.lib()
+    names = _declared_functions()
+    assert len(names) >= 18
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in rk._lib.SIGNATURES, f"{name} has no ctypes signature"
+        assert callable(getattr(rk, name, None)), f"binding lacks {name}"
+    assert rk.pred_version().startswith("rank_kv_block_amd")
+
+
+def _d(**kw):
+    base = dict(num_layers=32, num_q_heads=32, num_kv_heads=8, head_dim=128, r=32, block_size=16, max_blocks=8192)
+    base.update(kw)
+    return rk.PredDims(**base)
+
+
+@pytest.mark.parametrize("L,Hq,Hk,D,R,B,N,want", [
+    (1, 4, 1, 64, 16, 16, 64, 1 * 64 * 1 * 16 * 16 * 2),
+    (32, 32, 8, 128, 32, 16, 8192, 2 ** 31),
+    (1, 32, 8, 128, 32, 16, 131072, 2 ** 30),
+    (1, 32, 8, 128, 64, 16, 2048, 2 ** 25),
+    (64, 64, 8, 128, 64, 32, 32768, 68719476736),
+])
+def test_a_g_bytes(L, Hq, Hk, D, R, B, N, want):
+    assert rk.pred_a_g_bytes(rk.PredDims(L, Hq, Hk, D, R, B, N)) == want
+
+
+def test_invalid_dims():
+    with pytest.raises(rk.PredError) as e:
+        rk.pred_a_g_bytes(_d(num_q_heads=30, num_kv_heads=8))
+    assert e.value.code == rk.PRED_ERR_INVALID_DIMS
+    assert "multiple of num_kv_heads" in str(e.value)
+    for field in ["num_layers", "num_q_heads", "num_kv_heads", "head_dim", "r", "block_size", "max_blocks"]:
+        with pytest.raises(rk.PredError) as e:
+            rk.pred_a_g_bytes(_d(**{field: 0}))
+        assert e.value.code == rk.PRED_ERR_INVALID_DIMS
+    with pytest.raises(rk.PredError) as e:
+        rk.pred_a_g_bytes(_d(max_blocks=2 ** 62))
+    assert e.value.code == rk.PRED_ERR_INVALID_DIMS and "overflow" in str(e.value)
+
+
+def test_check_fit_margin_and_message():
+    d = _d()
+    need = rk.pred_a_g_bytes(d)
+    # fits when A_g is at most 95% of free memory
+    free_ok = need * 100 // 95 + 100
+    assert rk.pred_check_fit(d, free_ok) == 0
+    with pytest.raises(rk.PredError) as e:
+        rk.pred_check_fit(d, need)
+    assert e.value.code == rk.PRED_ERR_OOM
+    msg = str(e.value)
+    for fragment in ["r = 32", "r = 16", "halves A_g", "max_blocks = 8192", "num_layers (32)", "x 2"]:
+        assert fragment in msg, fragment
+    assert rk.pred_check_fit(d, 2 ** 64 - 1) == 0     # no overflow in the 95% budget
+
+
+def test_create_rejects_before_touching_a_device():
+    with pytest.raises(rk.PredError) as e:
+        rk.pred_create(_d(num_q_heads=12, num_kv_heads=8), 1, stream=0)
+    assert e.value.code == rk.PRED_ERR_INVALID_DIMS
+    with pytest.raises(rk.PredError) as e:
+        rk.pred_create(_d(r=12), 1, stream=0)
+    assert e.value.code == rk.PRED_ERR_UNSUPPORTED
+    with pytest.raises(rk.PredError) as e:
+        rk.pred_create(_d(head_dim=100), 1, stream=0)
+    assert e.value.code == rk.PRED_ERR_UNSUPPORTED
+
+
+def test_null_handle_errors():
+    lib = rk.lib()
+    assert lib.pred_project_q(None, None, 1, None, None) == rk.PRED_ERR_NULL_ARG
+    assert "NULL" in rk.pred_last_error()
+    assert lib.pred_project_kv_block(None, 0, 1, None, None, 1, None) == rk.PRED_ERR_NULL_ARG
+    assert lib.pred_score_blocks(None, 0, 1, None, 1, None, 1, 1, None, None) == rk.PRED_ERR_NULL_ARG
+    assert lib.pred_rank_victims(None, None, 1, 1, None, None, 0, None) == rk.PRED_ERR_NULL_ARG
+    assert lib.pred_device_error(None, None) == rk.PRED_ERR_NULL_ARG
+    assert lib.pred_a_g_ptr(None) is None
+    lib.pred_destroy(None)
+
+
+def test_rank_workspace_sizes():
+    assert rk.pred_rank_workspace_bytes(8192, 32) == 0
+    assert rk.pred_rank_workspace_bytes(16384, 1) == 0
+    assert rk.pred_rank_workspace_bytes(32768, 1) == 2 * 32768 * 8
+    assert rk.pred_rank_workspace_bytes(20000, 3) == 2 * 20000 * 3 * 8
+    assert rk.pred_rank_workspace_bytes(0, 5) == 0
+
+
+@pytest.mark.parametrize("D,R,seed", [(64, 16, 1001), (128, 32, 1002), (128, 64, 1004), (16, 8, 0),
+                                      (8, 8, 2 ** 64 - 1)])
+def test_library_projection_equals_oracle_generator(D, R, seed):
+    """Two independent implementations of the same seeded rule agree bit for bit."""
+    got = rk.pred_projection_host(D, R, seed)
+    want = prng.projection(D, R, seed)
+    assert got.dtype == np.uint16 and got.shape == (D, R)
+    assert np.array_equal(got, want)
+
+
+def test_limits_text():
+    t = rk.pred_limits()
+    assert "multiples of 8" in t and "r <= 256" in t

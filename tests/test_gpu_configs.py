@@ -1,0 +1,118 @@
+"""GPU parity on the five synthetic workloads at their real sizes, in the launch configuration
+bench.py times (Workload.step), against the oracle: full where the oracle finishes in seconds,
+on sampled blocks otherwise, plus exact checks of the whole ranking."""
+
+import numpy as np
+import pytest
+
+from oracle import predictor
+from tests.devmem import a_g_layer
+from tests.parity import assert_ranking, assert_scores, assert_ulp
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _bits(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def _check_workload(name, l0=0, sample_blocks=128, full_layers=1, keep_per_layer=8, steps=2):
+    from rank_kv_block_amd.workloads import CONFIGS, Workload
+    import rank_kv_block_amd as rk
+    c = CONFIGS[name]
+    rng = np.random.default_rng(c.index)
+    nl = c.step_layers
+    layers = list(range(l0, l0 + nl))
+    keep = set()
+    for l in layers:
+        for s in range(c.S):
+            for b in rng.choice(c.n, min(c.n, keep_per_layer), replace=False):
+                keep.add((l, s, int(b)))
+            keep.add((l, s, c.n - 1))          # the block each step re-projects
+    _say(name, "setup")
+    wl = Workload(c, keep=keep)
+    try:
+        _say(name, "steps", steps)
+        for _ in range(steps):
+            wl.step(l0)
+        torch.cuda.synchronize()
+        rk.pred_device_error(wl.h)
+        P = rk.pred_copy_projection(wl.h)
+
+        # q_proj: every element
+        qp = _bits(wl.q_proj)
+        assert_ulp(qp, predictor.project_q(_bits(wl.q[l0:l0 + nl]), P), f"{name} q_proj")
+
+        scores = wl.scores.cpu().numpy()
+        victims = wl.victims.cpu().numpy()
+        phys = wl.phys.numpy()
+        for li, l in enumerate(layers):
+            a_layer = a_g_layer(wl.h, wl.d, l)
+            # A_g: kept blocks against the oracle's projection of their keys
+            kept = [(s, b) for (kl, s, b) in wl.kept if kl == l]
+            if kept:
+                k = np.stack([wl.kept[(l, s, b)].view(torch.int16).numpy().view(np.uint16) for s, b in kept])
+                want = predictor.project_kv_slots(k, P)
+                got = np.stack([a_layer[phys[s, b]] for s, b in kept])
+                assert_ulp(got, want, f"{name} A_g layer {l}")
+            for s in range(c.S):
+                slots = a_layer[phys[s]]                     # [n, Hk, B, R] in logical order
+                if li < full_layers and s < 2:
+                    want = predictor.score_one(qp[li, s], slots)
+                    assert_scores(scores[li, s], want, c.R, f"{name} scores l{l} s{s}")
+                    assert_ranking(victims[li * c.S + s][None], scores[li, s][None], want[None], c.R,
+                                   f"{name} victims l{l} s{s}")
+                else:
+                    idx = np.sort(rng.choice(c.n, min(c.n, sample_blocks), replace=False))
+                    want = predictor.score_one(qp[li, s], slots[idx])
+                    assert_scores(scores[li, s, idx], want, c.R, f"{name} sampled scores l{l} s{s}")
+        # ranking (i) on every row: exact against the oracle's sort of the GPU's scores
+        want_v = predictor.rank_victims(scores.reshape(nl * c.S, c.n))
+        assert np.array_equal(victims, want_v), f"{name}: ranking differs from the oracle's sort"
+        if c.planted:
+            # planted keys are 4 x the group's first query head: their low-rank rows are exactly 4 x q_proj
+            for li, l in enumerate(layers):
+                a_layer = a_g_layer(wl.h, wl.d, l)
+                for b in wl.planted[:8]:
+                    slot = a_layer[phys[0, b]]
+                    for kv in range(c.Hk):
+                        want4 = predictor.bf16.encode(predictor.bf16.decode(qp[li, 0, 0, kv * c.g]) * 4.0)
+                        assert np.array_equal(slot[kv], np.broadcast_to(want4, slot[kv].shape)), (l, b, kv)
+            planted = sorted(wl.planted)
+            for row in range(nl * c.S):
+                assert victims[row, -c.planted:].tolist() == planted, f"{name}: planted blocks not last (row {row})"
+    finally:
+        wl.close()
+
+
+def test_config_tiny():
+    _check_workload("tiny", full_layers=1, keep_per_layer=64)
+
+
+def test_config_llama3_8b_decode():
+    _check_workload("llama3_8b_decode", full_layers=2, sample_blocks=96, keep_per_layer=8)
+
+
+def test_config_batched_decode():
+    _check_workload("batched_decode", full_layers=1, sample_blocks=64, keep_per_layer=2)
+
+
+def test_config_prefill_chunk():
+    _check_workload("prefill_chunk", full_layers=0, sample_blocks=48, keep_per_layer=16)
+
+
+def test_config_long_context_70b():
+    _check_workload("long_context_70b", l0=5, full_layers=1, keep_per_layer=16)

@@ -1,0 +1,248 @@
+"""GPU parity of every kernel against the oracle on small and ragged shapes (through the C ABI)."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import rank_kv_block_amd as rk
+from oracle import bf16, predictor, prng
+from tests.parity import assert_ranking, assert_scores, assert_ulp
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _bits_np(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+
+def _read_slots(h, d, pairs):
+    """A_g [L, N, Hk, B, R] with the listed (layer, slot) pairs read from the device, zeros elsewhere."""
+    a = np.zeros((d.num_layers, d.max_blocks, d.num_kv_heads, d.block_size, d.r), np.uint16)
+    for l, b in pairs:
+        a[l, b] = rk.pred_read_slot(h, l, b)
+    return a
+
+
+def _randn_bits(rng, shape, scale=1.0):
+    return bf16.encode(rng.standard_normal(shape) * scale)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rk.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- projection P
+
+@pytest.mark.parametrize("D,R,seed", [(64, 16, 1001), (128, 32, 1002), (128, 64, 1005)])
+def test_projection_on_device_matches_oracle(D, R, seed):
+    _say("P", D, R, seed)
+    d = rk.dims(1, 8, 8, D, R, 16, 4)
+    with rk.Predictor(d, seed) as p:
+        assert np.array_equal(rk.pred_copy_projection(p.handle), prng.projection(D, R, seed))
+
+
+# ---------------------------------------------------------------- hand examples
+
+def _pad(a, shape):
+    out = np.zeros(shape, dtype=np.float64)
+    out[tuple(slice(0, s) for s in np.shape(a))] = a
+    return out
+
+
+def test_hand_examples_on_gpu(golden_dir):
+    """Hand-worked values, zero-padded to head_dim = r = 8 (padding adds exact zeros)."""
+    for name in ["hand_a1.json", "hand_a2.json"]:
+        _say("hand", name)
+        g = json.load(open(os.path.join(golden_dir, name)))
+        dm = g["dims"]
+        Hq, Hk, B, N = dm["num_q_heads"], dm["num_kv_heads"], dm["block_size"], dm["max_blocks"]
+        d = rk.dims(1, Hq, Hk, 8, 8, B, N)
+        P = bf16.encode(_pad(g["P"], (8, 8)))
+        with rk.Predictor(d, projection=P, flags=rk.PRED_FLAG_ZERO_AG) as p:
+            q = _to_dev(bf16.encode(_pad(g["q"], (Hq, 8))))
+            qp = torch.empty((1, 1, 1, Hq, 8), dtype=torch.bfloat16, device="cuda")
+            rk.pred_project_q(p.handle, q, qp)
+            kb = np.array(g["k_blocks"] if "k_blocks" in g else [g["k_block"]], dtype=np.float64)
+            k = _to_dev(bf16.encode(_pad(kb, kb.shape[:-1] + (8,))))
+            rk.pred_project_kv_block(p.handle, 0, k.view(1, *k.shape))
+            scores = torch.empty((1, 1, N), dtype=torch.float32, device="cuda")
+            rk.pred_score_blocks(p.handle, 0, qp, None, scores)
+            vic = torch.empty((1, N), dtype=torch.int32, device="cuda")
+            rk.pred_rank_victims(p.handle, scores.view(1, N), vic)
+            torch.cuda.synchronize()
+            qpf = bf16.decode(_bits_np(qp)).reshape(Hq, 8)
+            assert np.array_equal(qpf[:, :2], np.array(g["q_proj"], float)) and not qpf[:, 2:].any()
+            slot0 = bf16.decode(rk.pred_read_slot(p.handle, 0, 0))[:, :, :2]
+            s = scores.cpu().numpy().reshape(N)
+            if name == "hand_a1.json":
+                assert np.array_equal(slot0, np.array(g["a_slots"][0], float))
+                assert s.tolist() == g["scores"]
+                assert vic.cpu().numpy()[0].tolist() == g["victims"]
+            else:
+                assert slot0.ravel().tolist() == g["a_slot_flat"]
+                assert s.tolist() == [g["score"]]
+
+
+# ---------------------------------------------------------------- random shapes
+
+SHAPES = [
+    # L, Hq, Hk, D, R, B, N, n, S, M, table
+    (2, 4, 1, 64, 16, 16, 70, 67, 1, 1, "perm"),          # C1-like, ragged
+    (3, 32, 8, 128, 32, 16, 300, 150, 2, 1, "perm"),       # C2-like, two sequences
+    (1, 64, 8, 128, 64, 32, 100, 97, 1, 1, "identity"),    # C5-like
+    (1, 32, 8, 128, 64, 16, 90, 90, 1, 1, "perm"),         # C4 dims at one row
+    (2, 8, 8, 64, 32, 16, 64, 41, 1, 2, "perm"),           # g = 1, two rows
+    (1, 16, 2, 64, 128, 8, 40, 33, 3, 1, "perm"),          # r = 128, short blocks
+    (1, 16, 4, 128, 32, 16, 64, 37, 1, 3, "identity"),     # 3 rows x g=4 -> 12 heads, padded to 16
+    (1, 32, 8, 128, 64, 16, 64, 23, 1, 17, "perm"),        # 17 rows: many-row path
+    (1, 12, 4, 64, 24, 16, 30, 30, 1, 1, "perm"),          # r = 24: plain per-block kernel
+    (1, 8, 2, 32, 16, 12, 30, 29, 2, 1, "identity"),       # block_size 12: plain per-block kernel
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"L{s[0]}-q{s[1]}-kv{s[2]}-d{s[3]}-r{s[4]}-b{s[5]}-n{s[7]}"
+                                              f"-S{s[8]}-M{s[9]}" for s in SHAPES])
+def test_random_shape_parity(shape):
+    L, Hq, Hk, D, R, B, N, n, S, M, table = shape
+    _say("shape", shape)
+    rng = np.random.default_rng([x for x in shape if isinstance(x, int)])
+    d = rk.dims(L, Hq, Hk, D, R, B, N)
+    seed = int(rng.integers(0, 2 ** 63))
+    with rk.Predictor(d, seed, flags=rk.PRED_FLAG_ZERO_AG) as p:
+        P = prng.projection(D, R, seed)
+        # tables: S disjoint slices of one permutation (or the identity)
+        if table == "perm":
+            perm = rng.permutation(N)[: S * n].reshape(S, n).astype(np.int32)
+        else:
+            assert S * n <= N
+            perm = np.arange(S * n, dtype=np.int32).reshape(S, n) if S > 1 else None
+        phys = perm if perm is not None else np.arange(n, dtype=np.int32)[None]
+        k = _randn_bits(rng, (L, S * n, B, Hk, D))
+        ktab = np.broadcast_to(phys.reshape(1, S * n), (L, S * n)).copy()
+        rk.pred_project_kv_block(p.handle, 0, _to_dev(k), _to_dev(ktab.view(np.int32)))
+        q = _randn_bits(rng, (L, S, M, Hq, D))
+        qp = torch.empty((L, S, M, Hq, R), dtype=torch.bfloat16, device="cuda")
+        rk.pred_project_q(p.handle, _to_dev(q), qp)
+        scores = torch.empty((L, S, n), dtype=torch.float32, device="cuda")
+        tab_dev = _to_dev(perm) if perm is not None else None
+        rk.pred_score_blocks(p.handle, 0, qp, tab_dev, scores)
+        vic = torch.empty((L * S, n), dtype=torch.int32, device="cuda")
+        ws_b = rk.pred_rank_workspace_bytes(n, L * S)
+        ws = torch.empty((ws_b // 8 + 1,), dtype=torch.int64, device="cuda") if ws_b else None
+        rk.pred_rank_victims(p.handle, scores.view(L * S, n), vic, ws)
+        rk.pred_device_error(p.handle)
+
+        # projections
+        assert_ulp(_bits_np(qp), predictor.project_q(q, P), "q_proj")
+        a_g = _read_slots(p.handle, d, [(l, int(b)) for l in range(L) for b in phys.reshape(-1)])
+        want_slots = predictor.project_kv_slots(k.reshape(L * S * n, B, Hk, D), P).reshape(L, S * n, Hk, B, R)
+        got_slots = np.stack([a_g[l][phys.reshape(-1)] for l in range(L)])
+        assert_ulp(got_slots, want_slots, "A_g")
+        # scores from the GPU's own q_proj and A_g
+        want = predictor.score_blocks(_bits_np(qp), a_g, 0, phys if perm is not None else None, n)
+        got = scores.cpu().numpy()
+        assert_scores(got, want, R)
+        assert_ranking(vic.cpu().numpy(), got.reshape(L * S, n), want.reshape(L * S, n), R)
+
+
+# ---------------------------------------------------------------- ranking
+
+@pytest.mark.parametrize("n,segs", [(1, 1), (5, 3), (64, 1), (513, 2), (2048, 4), (8192, 2), (16384, 1),
+                                    (16385, 1), (40000, 2), (65536, 1)])
+def test_rank_exact(n, segs):
+    _say("rank", n, segs)
+    rng = np.random.default_rng(n * 7 + segs)
+    s = (rng.integers(-300, 300, size=(segs, n)) * 0.25).astype(np.float32)   # many ties
+    s[:, :: 97] = -0.0
+    s[:, 1:: 89] = 0.0
+    if n > 10:
+        s[0, 3] = np.nan
+        s[0, 5] = -np.inf
+        s[-1, -1] = np.inf
+    d = rk.dims(1, 1, 1, 8, 8, 1, 1)
+    with rk.Predictor(d, 1) as p:
+        sc = torch.from_numpy(s).cuda()
+        vic = torch.empty((segs, n), dtype=torch.int32, device="cuda")
+        ws_b = rk.pred_rank_workspace_bytes(n, segs)
+        ws = torch.empty((ws_b // 8 + 1,), dtype=torch.int64, device="cuda") if ws_b else None
+        rk.pred_rank_victims(p.handle, sc, vic, ws)
+        got = vic.cpu().numpy()
+    assert np.array_equal(got, predictor.rank_victims(s))
+
+
+def test_rank_requires_workspace():
+    d = rk.dims(1, 1, 1, 8, 8, 1, 1)
+    with rk.Predictor(d, 1) as p:
+        sc = torch.zeros((1, 20000), dtype=torch.float32, device="cuda")
+        vic = torch.empty((1, 20000), dtype=torch.int32, device="cuda")
+        with pytest.raises(rk.PredError) as e:
+            rk.pred_rank_victims(p.handle, sc, vic, None)
+        assert e.value.code == rk.PRED_ERR_WORKSPACE
+
+
+# ---------------------------------------------------------------- error paths
+
+def test_invalid_table_entries_are_reported():
+    _say("invalid table")
+    d = rk.dims(1, 4, 2, 64, 16, 16, 8)
+    with rk.Predictor(d, 3, flags=rk.PRED_FLAG_ZERO_AG) as p:
+        rng = np.random.default_rng(0)
+        k = _to_dev(_randn_bits(rng, (1, 3, 16, 2, 64)))
+        bad = torch.tensor([[0, 9, 2]], dtype=torch.int32, device="cuda")
+        rk.pred_project_kv_block(p.handle, 0, k, bad)
+        with pytest.raises(rk.PredError) as e:
+            rk.pred_device_error(p.handle)
+        assert e.value.code == rk.PRED_ERR_DEVICE
+        rk.pred_device_error(p.handle)          # cleared
+        qp = torch.zeros((1, 1, 1, 4, 16), dtype=torch.bfloat16, device="cuda")
+        scores = torch.empty((1, 1, 3), dtype=torch.float32, device="cuda")
+        rk.pred_score_blocks(p.handle, 0, qp, torch.tensor([[0, -1, 2]], dtype=torch.int32, device="cuda"), scores)
+        with pytest.raises(rk.PredError):
+            rk.pred_device_error(p.handle)
+        s = scores.cpu().numpy().ravel()
+        assert np.isnan(s[1]) and s[0] == 0.0 and s[2] == 0.0
+
+
+def test_host_side_range_errors():
+    d = rk.dims(2, 4, 2, 64, 16, 16, 8)
+    with rk.Predictor(d, 3) as p:
+        k = torch.zeros((1, 1, 16, 2, 64), dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(rk.PredError) as e:
+            rk.pred_project_kv_block(p.handle, 2, k)
+        assert e.value.code == rk.PRED_ERR_OUT_OF_RANGE
+        qp = torch.zeros((2, 1, 1, 4, 16), dtype=torch.bfloat16, device="cuda")
+        sc = torch.empty((2, 1, 9), dtype=torch.float32, device="cuda")
+        with pytest.raises(rk.PredError) as e:
+            rk.pred_score_blocks(p.handle, 0, qp, None, sc)        # 9 blocks > max_blocks without a table
+        assert e.value.code == rk.PRED_ERR_OUT_OF_RANGE
+        with pytest.raises(rk.PredError) as e:
+            rk.pred_score_blocks(p.handle, 1, qp, None, sc[:, :, :4].contiguous())   # layers 1..2 of 2
+        assert e.value.code == rk.PRED_ERR_OUT_OF_RANGE
+
+
+def test_oom_is_reported_before_allocation():
+    free, _ = torch.cuda.mem_get_info()
+    # A_g sized at the whole free memory: above the 95% budget
+    per_block = 8 * 16 * 64 * 2
+    d = rk.dims(1, 8, 8, 128, 64, 16, free // per_block)
+    with pytest.raises(rk.PredError) as e:
+        rk.pred_create(d, 1)
+    assert e.value.code == rk.PRED_ERR_OOM
+    assert "halves A_g" in str(e.value)
