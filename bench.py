@@ -99,6 +99,8 @@ def main():
     ap.add_argument("--config", default="llama3_8b_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run one plain device copy of MIB MiB (a known-size reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the predictor's path has no multi-GPU part here); "
@@ -114,6 +116,14 @@ def main():
     torch.cuda.set_device(0)
     print(f"[bench] setting up {c.name}: {c.description}", file=sys.stderr, flush=True)
     wl = Workload(c)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print("[bench] warmup", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         wl.step(wl.layer0_for_step(i))

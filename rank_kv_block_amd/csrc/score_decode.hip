@@ -100,29 +100,43 @@ struct DecodeGeom {
     int SPB;               // load slots per block (U / 64 when U >= 64, else 1)
     int n_eff;             // effective heads per kv head = M * g
     int n_groups;          // ceil(n_eff / QH)
-    int64_t waves_per_seq;
-    int64_t total_waves;
+    int q_chunks;          // 16-byte chunks of one (layer, sequence) q_proj slab [M, Hq, R]
+    int64_t wgs_per_seq;   // workgroups per (layer, sequence); a workgroup never spans two
 };
 
-template <int LPR, int QH, int NS>
+constexpr int kWaves = 4;
+
+// QLDS: the (layer, sequence) q_proj slab is staged in LDS once per workgroup
+// and every wave reads its query fragments from there, which keeps the vector
+// memory pipeline for A_g alone.
+template <int LPR, int QH, int NS, bool QLDS, typename Off>
 __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
+    extern __shared__ uint4 q_lds[];
     const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wave >= gm.total_waves) return;
-    const int64_t wb = wave % gm.waves_per_seq;
-    const int64_t ls = wave / gm.waves_per_seq;
+    const int64_t wgb = blockIdx.x % gm.wgs_per_seq;
+    const int64_t ls = blockIdx.x / gm.wgs_per_seq;
     const int s = (int)(ls % a.S);
     const int l = (int)(ls / a.S);
-    const int64_t b_first = wb * gm.NBW;
+    const int64_t b_first = (wgb * kWaves + (threadIdx.x >> 6)) * gm.NBW;
+    const uint16_t* qrows = a.qp + ((int64_t)l * a.S + s) * (int64_t)a.M * a.Hq * a.R;
+    if constexpr (QLDS) {
+        const uint4* src = reinterpret_cast<const uint4*>(qrows);
+        for (int i = threadIdx.x; i < gm.q_chunks; i += 256) q_lds[i] = src[i];
+        __syncthreads();
+    }
+    if (b_first >= a.n) return;   // after the only barrier
     const int p = lane & (LPR - 1);
     const int g = a.Hq / a.Hk;
     const int64_t layer = a.layer0 + l;
     const int64_t slot_elems = (int64_t)a.Hk * a.B * a.R;
 
-    // Per load slot: the lane's row of its block's region (kv head 0).  Slots
-    // past the end or with an invalid table entry read A_g's first row instead
-    // (always mapped) and are masked out of the max, so the loads need no branch.
-    const uint16_t* base[NS];
+    // Per load slot: byte offset, within this layer's A_g slab, of the lane's
+    // row of its block's region at kv head 0.  Slots past the end or with an
+    // invalid table entry read the slab's first row instead and are masked out
+    // of the max, so the loads need no branch.  With 32-bit offsets the loads
+    // take the uniform slab base from SGPRs and one VGPR per slot.
+    const char* slab = reinterpret_cast<const char*>(a.ag + layer * a.N * slot_elems);
+    Off voff[NS];
     uint32_t live = 0;
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl) {
@@ -130,11 +144,11 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a, DecodeGe
         const int bi = f >> gm.log2U;
         const int t = (f & (gm.U - 1)) / LPR;
         const int64_t b = b_first + bi;
-        base[sl] = a.ag + p * 8;
+        voff[sl] = (Off)(p * 16);
         if (bi < gm.NBW && b < a.n) {
             const int64_t phys = a.tables ? (int64_t)a.tables[(int64_t)s * a.n + b] : b;
             if (phys >= 0 && phys < a.N) {
-                base[sl] = a.ag + (layer * a.N + phys) * slot_elems + (int64_t)t * a.R + p * 8;
+                voff[sl] = (Off)((phys * slot_elems + (int64_t)t * a.R + p * 8) * 2);
                 live |= 1u << sl;
             }
         }
@@ -144,12 +158,22 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a, DecodeGe
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl) rm[sl] = -__builtin_inff();
 
-    const uint16_t* qrows = a.qp + ((int64_t)l * a.S + s) * (int64_t)a.M * a.Hq * a.R;
     const int fx = label_xor<LPR, QH>(p);
     const int64_t kv_stride = (int64_t)a.B * a.R;
+    auto load_a = [&](uint4 (&dst)[NS], int kv) {
+        // dead slots read inside the slab's first slot
+        const char* kbase = slab + kv * kv_stride * 2;
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) dst[sl] = *reinterpret_cast<const uint4*>(kbase + voff[sl]);
+    };
 
+    // A_g loads run one kv head ahead of the arithmetic.
+    uint4 av[NS], an[NS];
+    load_a(av, 0);
     for (int hg = 0; hg < gm.n_groups; ++hg) {
         for (int kv = 0; kv < a.Hk; ++kv) {
+            const bool more = (kv + 1 < a.Hk) || (hg + 1 < gm.n_groups);
+            if (more) load_a(an, kv + 1 < a.Hk ? kv + 1 : 0);
             uint32_t q[QH][4];
 #pragma unroll
             for (int i = 0; i < QH; ++i) {
@@ -157,14 +181,12 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a, DecodeGe
                 if (e >= gm.n_eff) e = gm.n_eff - 1;  // padding: repeat a real head (max unchanged)
                 const int row = e / g;
                 const int h = e - row * g;
-                const uint4 w = *reinterpret_cast<const uint4*>(
-                    qrows + ((int64_t)row * a.Hq + kv * g + h) * a.R + p * 8);
+                const int64_t off = ((int64_t)row * a.Hq + kv * g + h) * a.R + p * 8;
+                uint4 w;
+                if constexpr (QLDS) w = q_lds[off >> 3];
+                else w = *reinterpret_cast<const uint4*>(qrows + off);
                 q[i][0] = w.x; q[i][1] = w.y; q[i][2] = w.z; q[i][3] = w.w;
             }
-            uint4 av[NS];
-#pragma unroll
-            for (int sl = 0; sl < NS; ++sl)
-                av[sl] = *reinterpret_cast<const uint4*>(base[sl] + ((live >> sl) & 1u ? kv * kv_stride : 0));
 #pragma unroll
             for (int sl = 0; sl < NS; ++sl) {
                 float v[QH];
@@ -181,6 +203,10 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a, DecodeGe
 #pragma unroll
                 for (int i = 1; i < rem; ++i) mx = fmaxf(mx, v[i]);
                 rm[sl] = ((live >> sl) & 1u) ? fmaxf(rm[sl], mx) : rm[sl];
+            }
+            if (more) {
+#pragma unroll
+                for (int sl = 0; sl < NS; ++sl) av[sl] = an[sl];
             }
         }
     }
@@ -271,10 +297,19 @@ int pick_qh(int n_eff) {
     return qh;
 }
 
+constexpr int kQLdsMaxBytes = 32768;
+
 template <int LPR, int QH, int NS>
 void launch_decode_t(const ScoreArgs& a, const DecodeGeom& gm, hipStream_t st) {
-    const unsigned grid = (unsigned)((gm.total_waves + 3) / 4);
-    score_decode_kernel<LPR, QH, NS><<<grid, 256, 0, st>>>(a, gm);
+    const unsigned grid = (unsigned)(gm.wgs_per_seq * a.S * a.n_layers);
+    const int q_bytes = gm.q_chunks * 16;
+    const bool narrow = a.N * (int64_t)a.Hk * a.B * a.R * 2 < (int64_t(1) << 32);
+    if (q_bytes <= kQLdsMaxBytes && narrow)
+        score_decode_kernel<LPR, QH, NS, true, uint32_t><<<grid, 256, q_bytes, st>>>(a, gm);
+    else if (q_bytes <= kQLdsMaxBytes)
+        score_decode_kernel<LPR, QH, NS, true, uint64_t><<<grid, 256, q_bytes, st>>>(a, gm);
+    else
+        score_decode_kernel<LPR, QH, NS, false, uint64_t><<<grid, 256, 0, st>>>(a, gm);
 }
 
 template <int LPR, int NS>
@@ -314,8 +349,9 @@ bool decode_geometry(const ScoreArgs& a, DecodeGeom& gm, int& ns, int& lpr, int&
     gm.n_eff = a.M * g;
     qh = pick_qh(gm.n_eff);
     gm.n_groups = (gm.n_eff + qh - 1) / qh;
-    gm.waves_per_seq = (a.n + gm.NBW - 1) / gm.NBW;
-    gm.total_waves = gm.waves_per_seq * a.S * a.n_layers;
+    gm.q_chunks = (int)((int64_t)a.M * a.Hq * a.R / 8);
+    const int64_t waves_per_seq = (a.n + gm.NBW - 1) / gm.NBW;
+    gm.wgs_per_seq = (waves_per_seq + kWaves - 1) / kWaves;
     return true;
 }
 

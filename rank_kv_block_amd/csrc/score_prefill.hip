@@ -1,11 +1,206 @@
-// Many-row block scorer (prefill chunk): placeholder until the MFMA kernel lands.
+// Many-row block scorer for a prefill chunk (predictor.rs page, score_blocks,
+// with many query rows): the same score as the decode kernel,
+//   score[l, s, b] = max over rows i, heads h, tokens t of q_proj[l, s, i, h, :] . A[l, T[s, b], h / g, t, :]
+// but with M * g queries per kv head it is a real contraction: for kv head k,
+// Q_k [M*g, R] times A_k^T [R, n*B] followed by a max over the query axis and
+// over each block's B columns.  It runs on bf16 MFMA (v_mfma_f32_32x32x16_bf16,
+// f32 accumulation) with the max fused into the epilogue, so the [M*g, n*B]
+// product never leaves registers.
+//
+// Tiling: a workgroup owns one (layer, sequence, kv head) and 4 waves x NKT key
+// tiles of 32 keys (consecutive tokens of consecutive blocks).  A wave keeps its
+// keys as MFMA B operands in registers for the whole kernel and streams every
+// 32-query tile of its kv head as the A operand (the queries of one kv head are
+// at most a few MiB and stay in L2).  Each lane of the 32x32 f32 accumulator
+// holds one key column; the lane keeps a running max of its column over all
+// query tiles.  At the end the two lane halves are combined, then the 16 (or 8,
+// 32) lanes of one block, and the block's max goes to the score array with an
+// atomic max on an order-preserving uint32 key (kv heads sit in different
+// workgroups).  A fill kernel clears the keys first and a last kernel turns
+// them back into float32 in place.
+//
+// Workgroups are numbered kv-head fastest, so with 8 kv heads each XCD (which
+// takes every 8th workgroup) serves one kv head and its L2 holds one kv head's
+// queries.
 #include "common.h"
 #include "kernels.h"
 
 namespace pred {
 
-bool prefill_supported(const ScoreArgs&) { return false; }
+namespace {
 
-hipError_t launch_score_prefill(const ScoreArgs&, hipStream_t) { return hipErrorNotSupported; }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kWaves = 4;
+
+struct PrefillGeom {
+    int n_eff;            // queries per kv head = M * g
+    int q_tiles;          // ceil(n_eff / 32)
+    int64_t n_keys;       // n * B keys per sequence
+    int64_t groups;       // key groups per (layer, sequence, kv head)
+};
+
+template <int M>
+__device__ inline float lane_xor(float v) {
+    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+    if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+    if constexpr (M == 7) return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
+    if constexpr (M == 15) return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true));
+    return __shfl_xor(v, M);
+}
+
+__device__ inline bf16x8_t load8(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
+}
+
+template <int RS, int NKT, int BS>
+__global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, PrefillGeom gm, uint32_t* __restrict__ keys) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int kv = (int)(blockIdx.x % a.Hk);
+    int64_t rest = blockIdx.x / a.Hk;
+    const int64_t grp = rest % gm.groups;
+    rest /= gm.groups;
+    const int s = (int)(rest % a.S);
+    const int l = (int)(rest / a.S);
+    const int g = a.Hq / a.Hk;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int64_t key0 = (grp * kWaves + wave) * (NKT * 32);
+    if (key0 >= gm.n_keys) return;   // whole wave past the end (no barriers in this kernel)
+    const int64_t layer = a.layer0 + l;
+    const int64_t slot_elems = (int64_t)a.Hk * BS * a.R;
+
+    // B operands: this lane's key column of every key tile, R/16 k-steps of 8 values.
+    bf16x8_t kb[NKT][RS];
+    uint32_t live = 0;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) {
+        const int64_t key = key0 + t * 32 + col;
+        const uint16_t* src = a.ag;
+        if (key < gm.n_keys) {
+            const int64_t b = key / BS;
+            const int tok = (int)(key - b * BS);
+            const int64_t phys = a.tables ? (int64_t)a.tables[(int64_t)s * a.n + b] : b;
+            if (phys >= 0 && phys < a.N) {
+                src = a.ag + (layer * a.N + phys) * slot_elems + ((int64_t)kv * BS + tok) * a.R;
+                live |= 1u << t;
+            }
+        }
+#pragma unroll
+        for (int st = 0; st < RS; ++st) kb[t][st] = load8(src + st * 16 + half * 8);
+    }
+
+    float rm[NKT];
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) rm[t] = -__builtin_inff();
+
+    const uint16_t* qrows = a.qp + ((int64_t)l * a.S + s) * (int64_t)a.M * a.Hq * a.R;
+    auto q_src = [&](int qt) {
+        int e = qt * 32 + col;
+        if (e >= gm.n_eff) e = gm.n_eff - 1;   // padding rows repeat a real query
+        const int row = e / g;
+        const int h = e - row * g;
+        return qrows + ((int64_t)row * a.Hq + kv * g + h) * a.R + half * 8;
+    };
+    // A operands of the current query tile; the next tile's are loaded before
+    // the current tile's MFMAs so the load latency hides behind them.
+    bf16x8_t qa[RS], qn[RS];
+    {
+        const uint16_t* q0 = q_src(0);
+#pragma unroll
+        for (int st = 0; st < RS; ++st) qa[st] = load8(q0 + st * 16);
+    }
+    for (int qt = 0; qt < gm.q_tiles; ++qt) {
+        const uint16_t* qnext = q_src(qt + 1 < gm.q_tiles ? qt + 1 : qt);
+#pragma unroll
+        for (int st = 0; st < RS; ++st) qn[st] = load8(qnext + st * 16);
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) {
+            f32x16_t acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < RS; ++st) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], kb[t][st], acc, 0, 0, 0);
+            float m = fmaxf(acc[0], acc[1]);
+#pragma unroll
+            for (int i = 2; i < 16; ++i) m = fmaxf(m, acc[i]);
+            rm[t] = fmaxf(rm[t], m);
+        }
+#pragma unroll
+        for (int st = 0; st < RS; ++st) qa[st] = qn[st];
+    }
+
+    uint32_t* out = keys + ((int64_t)l * a.S + s) * a.n;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) {
+        float v = fmaxf(rm[t], lane_xor<32>(rm[t]));   // rows split across the two lane halves
+        v = fmaxf(v, lane_xor<1>(v));
+        v = fmaxf(v, lane_xor<2>(v));
+        if constexpr (BS >= 8) v = fmaxf(v, lane_xor<7>(v));
+        if constexpr (BS >= 16) v = fmaxf(v, lane_xor<15>(v));
+        if constexpr (BS >= 32) v = fmaxf(v, lane_xor<16>(v));
+        const int64_t key = key0 + t * 32 + col;
+        if (half == 0 && (col % BS) == 0 && key < gm.n_keys) {
+            if ((live >> t) & 1u) atomicMax(out + key / BS, order_key(v));
+            else if (kv == 0) atomicOr(a.err, DEVERR_TABLE);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// Keys back to float32 in place; a block no workgroup wrote (invalid table entry) becomes NaN.
+__global__ __launch_bounds__(256) void keys_to_scores_kernel(uint32_t* p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) reinterpret_cast<float*>(p)[i] = key_to_float(p[i]);
+}
+
+template <int RS, int NKT, int BS>
+void launch_t(const ScoreArgs& a, const PrefillGeom& gm, uint32_t* keys, hipStream_t st) {
+    const int64_t wgs = gm.groups * a.Hk * a.S * a.n_layers;
+    score_prefill_kernel<RS, NKT, BS><<<(unsigned)wgs, 256, 0, st>>>(a, gm, keys);
+}
+
+template <int RS, int NKT>
+void launch_bs(const ScoreArgs& a, const PrefillGeom& gm, uint32_t* keys, hipStream_t st) {
+    switch (a.B) {
+        case 8: launch_t<RS, NKT, 8>(a, gm, keys, st); break;
+        case 16: launch_t<RS, NKT, 16>(a, gm, keys, st); break;
+        default: launch_t<RS, NKT, 32>(a, gm, keys, st); break;
+    }
+}
+
+constexpr int kNKT = 4;
+
+}  // namespace
+
+bool prefill_supported(const ScoreArgs& a) {
+    return (a.R == 16 || a.R == 32 || a.R == 64 || a.R == 128) && (a.B == 8 || a.B == 16 || a.B == 32);
+}
+
+hipError_t launch_score_prefill(const ScoreArgs& a, hipStream_t st) {
+    PrefillGeom gm;
+    const int g = a.Hq / a.Hk;
+    gm.n_eff = a.M * g;
+    gm.q_tiles = (gm.n_eff + 31) / 32;
+    gm.n_keys = a.n * a.B;
+    const int64_t keys_per_group = (int64_t)kWaves * kNKT * 32;
+    gm.groups = (gm.n_keys + keys_per_group - 1) / keys_per_group;
+    uint32_t* keys = reinterpret_cast<uint32_t*>(a.scores);
+    const int64_t total = (int64_t)a.n_layers * a.S * a.n;
+    const unsigned fill_grid = (unsigned)((total + 255) / 256);
+    fill_u32_kernel<<<fill_grid, 256, 0, st>>>(keys, total, 0u);
+    switch (a.R) {
+        case 16: launch_bs<1, kNKT>(a, gm, keys, st); break;
+        case 32: launch_bs<2, kNKT>(a, gm, keys, st); break;
+        case 64: launch_bs<4, kNKT>(a, gm, keys, st); break;
+        default: launch_bs<8, kNKT>(a, gm, keys, st); break;
+    }
+    keys_to_scores_kernel<<<fill_grid, 256, 0, st>>>(keys, total);
+    return hipGetLastError();
+}
 
 }  // namespace pred

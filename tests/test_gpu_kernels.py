@@ -24,7 +24,13 @@ def _bits_np(t):
 
 
 def _to_dev(bits):
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+    """bf16 bit patterns (uint16) -> device int16 tensor."""
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).cuda()
+
+
+def _tab_dev(ids):
+    """Block ids -> device int32 tensor."""
+    return torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
 
 
 def _read_slots(h, d, pairs):
@@ -113,7 +119,12 @@ SHAPES = [
     (1, 16, 4, 128, 32, 16, 64, 37, 1, 3, "identity"),     # 3 rows x g=4 -> 12 heads, padded to 16
     (1, 32, 8, 128, 64, 16, 64, 23, 1, 17, "perm"),        # 17 rows: many-row path
     (1, 12, 4, 64, 24, 16, 30, 30, 1, 1, "perm"),          # r = 24: plain per-block kernel
-    (1, 8, 2, 32, 16, 12, 30, 29, 2, 1, "identity"),       # block_size 12: plain per-block kernel
+    (1, 8, 2, 32, 16, 12, 60, 29, 2, 1, "identity"),       # block_size 12: plain per-block kernel
+    # many query rows: the MFMA scorer
+    (1, 32, 8, 128, 64, 16, 300, 260, 1, 64, "perm"),      # prefill-chunk dims, ragged key tiles
+    (2, 16, 4, 64, 32, 32, 150, 70, 2, 40, "perm"),        # block_size 32, two layers, two sequences
+    (1, 8, 1, 64, 16, 8, 50, 45, 1, 33, "identity"),       # block_size 8, r = 16, one kv head
+    (1, 16, 2, 128, 128, 16, 40, 33, 1, 9, "perm"),        # r = 128, 72 queries per kv head
 ]
 
 
@@ -136,12 +147,12 @@ def test_random_shape_parity(shape):
         phys = perm if perm is not None else np.arange(n, dtype=np.int32)[None]
         k = _randn_bits(rng, (L, S * n, B, Hk, D))
         ktab = np.broadcast_to(phys.reshape(1, S * n), (L, S * n)).copy()
-        rk.pred_project_kv_block(p.handle, 0, _to_dev(k), _to_dev(ktab.view(np.int32)))
+        rk.pred_project_kv_block(p.handle, 0, _to_dev(k), _tab_dev(ktab))
         q = _randn_bits(rng, (L, S, M, Hq, D))
         qp = torch.empty((L, S, M, Hq, R), dtype=torch.bfloat16, device="cuda")
         rk.pred_project_q(p.handle, _to_dev(q), qp)
         scores = torch.empty((L, S, n), dtype=torch.float32, device="cuda")
-        tab_dev = _to_dev(perm) if perm is not None else None
+        tab_dev = _tab_dev(perm) if perm is not None else None
         rk.pred_score_blocks(p.handle, 0, qp, tab_dev, scores)
         vic = torch.empty((L * S, n), dtype=torch.int32, device="cuda")
         ws_b = rk.pred_rank_workspace_bytes(n, L * S)
@@ -214,6 +225,13 @@ def test_invalid_table_entries_are_reported():
         qp = torch.zeros((1, 1, 1, 4, 16), dtype=torch.bfloat16, device="cuda")
         scores = torch.empty((1, 1, 3), dtype=torch.float32, device="cuda")
         rk.pred_score_blocks(p.handle, 0, qp, torch.tensor([[0, -1, 2]], dtype=torch.int32, device="cuda"), scores)
+        with pytest.raises(rk.PredError):
+            rk.pred_device_error(p.handle)
+        s = scores.cpu().numpy().ravel()
+        assert np.isnan(s[1]) and s[0] == 0.0 and s[2] == 0.0
+        # the many-row scorer reports it the same way
+        qm = torch.zeros((1, 1, 9, 4, 16), dtype=torch.bfloat16, device="cuda")
+        rk.pred_score_blocks(p.handle, 0, qm, torch.tensor([[0, 8, 2]], dtype=torch.int32, device="cuda"), scores)
         with pytest.raises(rk.PredError):
             rk.pred_device_error(p.handle)
         s = scores.cpu().numpy().ravel()
