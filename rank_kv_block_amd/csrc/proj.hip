@@ -1,17 +1,21 @@
 // Projection kernels: Q @ P and K @ P with float64 accumulation and one RNE
 // rounding to bf16 (predictor.rs page: project_q, project_kv_block).
 //
-// One lane owns one input vector (D bf16) and RC of its R outputs.  Products
-// of two bf16 values are exact in float64 and a float64 sum of head_dim of them
-// loses nothing for realistic data, so the output is the correctly rounded
-// bf16 of the exact dot product; a float32 accumulator would miss that by more
-// than one bf16 ulp for outputs near zero.
+// Products of two bf16 values are exact in float64 and a float64 sum of
+// head_dim of them loses nothing for realistic data, so every output is the
+// correctly rounded bf16 of the exact dot product; a float32 accumulator would
+// miss that by more than one bf16 ulp for outputs near zero.
 //
-// P is read as float64 [D, R] (converted once at create time) through the
-// scalar data cache: every lane of a wave needs the same P element at the same
-// time, so the compiler issues uniform scalar loads and the FMAs take P from
-// SGPRs.  A copy in LDS would cost one 8-byte return per lane per FMA from
-// the LDS, four times the fp64 FMA rate of the CU.
+// Main path: float64 MFMA (v_mfma_f64_16x16x4_f64).  A wave owns 16 output
+// columns and keeps the matching slice of P as B operands in registers (lane
+// group q = lane / 16 takes the head_dim range [q*D/4, (q+1)*D/4), one value
+// per k-step), then streams tiles of 16 input vectors as A operands, converted
+// bf16 -> float64 on the fly.  Each 16x16 float64 tile is rounded to bf16 in
+// the epilogue and written either densely (project_q) or into the A_g slot the
+// block table names, transposing [B, Hk] -> [Hk, B] (project_kv_block).
+//
+// Fallback (head_dim not in {32, 64, 128, 256} or r not a multiple of 16): one
+// lane per vector with float64 FMAs, P read through the scalar cache.
 #include "common.h"
 #include "kernels.h"
 
@@ -93,6 +97,115 @@ __global__ __launch_bounds__(256) void project_paged_kernel(
     project_vector<RC>(k + v * D, pf, D, R, j0, dst);
 }
 
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+// Where the projection of input vector `row` goes.
+struct OutMap {
+    uint16_t* out;          // dense: [n_vec, R]; paged: first layer's A_g slab
+    const int32_t* table;   // paged: [n_layers, n_blocks] or null (identity)
+    uint32_t* err;
+    int64_t n_blocks, N;
+    int Hk, B, R;
+    bool paged;
+
+    // Element offset of the row's output, or -1 when its table entry is invalid.
+    __device__ inline int64_t row_offset(int64_t row) const {
+        if (!paged) return row * R;
+        const int64_t per_block = (int64_t)B * Hk;
+        const int64_t li = row / per_block;
+        const int rem = (int)(row - li * per_block);
+        const int t = rem / Hk;
+        const int kv = rem - t * Hk;
+        const int64_t l = li / n_blocks;
+        const int64_t phys = table ? (int64_t)table[li] : (li - l * n_blocks);
+        if (phys < 0 || phys >= N) return -1;
+        return (((l * N + phys) * Hk + kv) * B + t) * (int64_t)R;
+    }
+};
+
+template <int DG>
+__device__ inline void load_row_quarter(const uint16_t* in, int64_t row, int q, uint4 (&w)[DG / 8]) {
+    const uint4* src = reinterpret_cast<const uint4*>(in + row * (4 * DG) + q * DG);
+#pragma unroll
+    for (int c = 0; c < DG / 8; ++c) w[c] = src[c];
+}
+
+// unit = (vector group, 16-column tile); a vector group is VT tiles of 16 vectors.
+template <int DG>
+__global__ __launch_bounds__(256) void project_mfma_kernel(const uint16_t* __restrict__ in,
+                                                           const double* __restrict__ pf, OutMap om,
+                                                           int64_t n_vec, int VT, int64_t units) {
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (unit >= units) return;
+    const int R = om.R;
+    const int jtiles = R >> 4;
+    const int jt = (int)(unit % jtiles);
+    const int64_t vgrp = unit / jtiles;
+    const int col = lane & 15;
+    const int q = lane >> 4;
+    const int j = jt * 16 + col;
+
+    double pb[DG];   // B operands: P[q*DG + s][j]
+#pragma unroll
+    for (int s = 0; s < DG; ++s) pb[s] = pf[(int64_t)(q * DG + s) * R + j];
+
+    const int64_t v_first = vgrp * VT * 16;
+    if (v_first >= n_vec) return;
+    const int64_t v_end = (v_first + (int64_t)VT * 16) < n_vec ? (v_first + (int64_t)VT * 16) : n_vec;
+    auto clamp_row = [&](int64_t r) { return r < n_vec ? r : n_vec - 1; };  // tail rows are computed, not stored
+
+    uint4 w[DG / 8], wn[DG / 8];
+    load_row_quarter<DG>(in, clamp_row(v_first + col), q, w);
+    for (int64_t v0 = v_first; v0 < v_end; v0 += 16) {
+        if (v0 + 16 < v_end) load_row_quarter<DG>(in, clamp_row(v0 + 16 + col), q, wn);
+        f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int c = 0; c < DG / 8; ++c) {
+            const uint32_t ww[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_lo(ww[e]), pb[c * 8 + 2 * e], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_hi(ww[e]), pb[c * 8 + 2 * e + 1], acc, 0, 0, 0);
+            }
+        }
+        // acc[v] of lane group q is output (row v0 + q + 4v, column j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t row = v0 + q + 4 * v;
+            if (row < v_end) {
+                const int64_t off = om.row_offset(row);
+                if (off >= 0) om.out[off + j] = f64_to_bf16_rne(acc[v]);
+                else if (col == 0 && jt == 0) atomicOr(om.err, DEVERR_TABLE);
+            }
+        }
+        if (v0 + 16 < v_end) {
+#pragma unroll
+            for (int c = 0; c < DG / 8; ++c) w[c] = wn[c];
+        }
+    }
+}
+
+bool mfma_path(int D, int R) { return (D == 32 || D == 64 || D == 128 || D == 256) && R % 16 == 0; }
+
+hipError_t launch_mfma(const uint16_t* in, const double* pf, const OutMap& om, int64_t n_vec, int D,
+                       hipStream_t stream) {
+    const int64_t vtiles = (n_vec + 15) / 16;
+    const int jtiles = om.R / 16;
+    // about two waves per SIMD when there is that much work, one vector tile per wave otherwise
+    int64_t vt = (vtiles * jtiles) / 2048;
+    if (vt < 1) vt = 1;
+    const int64_t units = ((vtiles + vt - 1) / vt) * jtiles;
+    const unsigned grid = (unsigned)((units + 3) / 4);
+    switch (D) {
+        case 32: project_mfma_kernel<8><<<grid, 256, 0, stream>>>(in, pf, om, n_vec, (int)vt, units); break;
+        case 64: project_mfma_kernel<16><<<grid, 256, 0, stream>>>(in, pf, om, n_vec, (int)vt, units); break;
+        case 128: project_mfma_kernel<32><<<grid, 256, 0, stream>>>(in, pf, om, n_vec, (int)vt, units); break;
+        default: project_mfma_kernel<64><<<grid, 256, 0, stream>>>(in, pf, om, n_vec, (int)vt, units); break;
+    }
+    return hipGetLastError();
+}
+
 // Output chunk width: the widest of 64/32/16/8 that divides R, narrowed while
 // the grid would leave the 1024 SIMDs with fewer than ~4 waves each.
 int pick_rc(int R, int64_t n_vec) {
@@ -110,6 +223,10 @@ int pick_rc(int R, int64_t n_vec) {
 hipError_t launch_project_dense(const uint16_t* in, const double* pf, uint16_t* out, int64_t n_vec,
                                 int D, int R, hipStream_t stream) {
     if (n_vec <= 0) return hipSuccess;
+    if (mfma_path(D, R)) {
+        OutMap om{out, nullptr, nullptr, 0, 0, 0, 0, R, false};
+        return launch_mfma(in, pf, om, n_vec, D, stream);
+    }
     const int rc = pick_rc(R, n_vec);
     dim3 grid((unsigned)((n_vec + 255) / 256), (unsigned)(R / rc));
     switch (rc) {
@@ -126,6 +243,10 @@ hipError_t launch_project_paged(const uint16_t* k, const double* pf, uint16_t* a
                                 int B, int D, int R, uint32_t* err, hipStream_t stream) {
     const int64_t n_vec = (int64_t)n_layers * n_blocks * B * Hk;
     if (n_vec <= 0) return hipSuccess;
+    if (mfma_path(D, R)) {
+        OutMap om{a_first, table, err, n_blocks, N, Hk, B, R, true};
+        return launch_mfma(k, pf, om, n_vec, D, stream);
+    }
     const int rc = pick_rc(R, n_vec);
     dim3 grid((unsigned)((n_vec + 255) / 256), (unsigned)(R / rc));
 #define PRED_PAGED(RCV)                                                                                      \

@@ -103,7 +103,7 @@ def test_null_handle_errors():
 
 def test_rank_workspace_sizes():
     assert rk.pred_rank_workspace_bytes(8192, 32) == 0
-    assert rk.pred_rank_workspace_bytes(16384, 1) == 0
+    assert rk.pred_rank_workspace_bytes(8193, 1) == 2 * 8193 * 8
     assert rk.pred_rank_workspace_bytes(32768, 1) == 2 * 32768 * 8
     assert rk.pred_rank_workspace_bytes(20000, 3) == 2 * 20000 * 3 * 8
     assert rk.pred_rank_workspace_bytes(0, 5) == 0

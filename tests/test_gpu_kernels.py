@@ -115,7 +115,7 @@ SHAPES = [
     (1, 64, 8, 128, 64, 32, 100, 97, 1, 1, "identity"),    # C5-like
     (1, 32, 8, 128, 64, 16, 90, 90, 1, 1, "perm"),         # C4 dims at one row
     (2, 8, 8, 64, 32, 16, 64, 41, 1, 2, "perm"),           # g = 1, two rows
-    (1, 16, 2, 64, 128, 8, 40, 33, 3, 1, "perm"),          # r = 128, short blocks
+    (1, 16, 2, 64, 128, 8, 120, 33, 3, 1, "perm"),         # r = 128, short blocks
     (1, 16, 4, 128, 32, 16, 64, 37, 1, 3, "identity"),     # 3 rows x g=4 -> 12 heads, padded to 16
     (1, 32, 8, 128, 64, 16, 64, 23, 1, 17, "perm"),        # 17 rows: many-row path
     (1, 12, 4, 64, 24, 16, 30, 30, 1, 1, "perm"),          # r = 24: plain per-block kernel
@@ -175,8 +175,8 @@ def test_random_shape_parity(shape):
 
 # ---------------------------------------------------------------- ranking
 
-@pytest.mark.parametrize("n,segs", [(1, 1), (5, 3), (64, 1), (513, 2), (2048, 4), (8192, 2), (16384, 1),
-                                    (16385, 1), (40000, 2), (65536, 1)])
+@pytest.mark.parametrize("n,segs", [(1, 1), (5, 3), (64, 1), (513, 2), (2048, 4), (8192, 2), (8193, 1),
+                                    (16384, 1), (16385, 1), (24576, 3), (40000, 2), (65536, 1)])
 def test_rank_exact(n, segs):
     _say("rank", n, segs)
     rng = np.random.default_rng(n * 7 + segs)
@@ -194,6 +194,26 @@ def test_rank_exact(n, segs):
         ws_b = rk.pred_rank_workspace_bytes(n, segs)
         ws = torch.empty((ws_b // 8 + 1,), dtype=torch.int64, device="cuda") if ws_b else None
         rk.pred_rank_victims(p.handle, sc, vic, ws)
+        got = vic.cpu().numpy()
+    assert np.array_equal(got, predictor.rank_victims(s))
+
+
+@pytest.mark.parametrize("kind", ["all_equal", "low_bits", "two_values", "descending"])
+def test_rank_special_orders(kind):
+    _say("rank special", kind)
+    n = 3000
+    if kind == "all_equal":
+        s = np.full((2, n), 7.25, np.float32)
+    elif kind == "low_bits":     # keys that differ only in the last mantissa bits
+        s = (np.float32(1.0) + np.random.default_rng(1).integers(0, 16, (2, n)).astype(np.float32) * np.float32(2 ** -23))
+    elif kind == "two_values":
+        s = np.where(np.random.default_rng(2).random((2, n)) < 0.5, -1.5, 2.5).astype(np.float32)
+    else:
+        s = np.linspace(1000, -1000, 2 * n, dtype=np.float32).reshape(2, n)
+    d = rk.dims(1, 1, 1, 8, 8, 1, 1)
+    with rk.Predictor(d, 1) as p:
+        vic = torch.empty((2, n), dtype=torch.int32, device="cuda")
+        rk.pred_rank_victims(p.handle, torch.from_numpy(s).cuda(), vic)
         got = vic.cpu().numpy()
     assert np.array_equal(got, predictor.rank_victims(s))
 
