@@ -24,6 +24,21 @@
 #include "common.h"
 #include "kernels.h"
 
+// Tuning knobs (compile-time).  PRED_DECODE_AUX is the cache-policy field of
+// the streamed A_g buffer loads: 2 = nontemporal (A_g is read once per call,
+// so it should not displace q_proj, tables and other cached data), measured
+// 5-8% faster than the default policy.  WAVES_PER_EU caps registers for that
+// many waves per SIMD (0 = compiler's choice).
+#ifndef PRED_DECODE_AUX
+#define PRED_DECODE_AUX 2
+#endif
+#ifndef PRED_DECODE_NS_SMALL
+#define PRED_DECODE_NS_SMALL 8
+#endif
+#ifndef PRED_DECODE_WAVES_PER_EU
+#define PRED_DECODE_WAVES_PER_EU 0
+#endif
+
 namespace pred {
 
 namespace {
@@ -108,16 +123,24 @@ constexpr int kWaves = 4;
 
 // QLDS: the (layer, sequence) q_proj slab is staged in LDS once per workgroup
 // and every wave reads its query fragments from there, which keeps the vector
-// memory pipeline for A_g alone.
-template <int LPR, int QH, int NS, bool QLDS, typename Off>
-__global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
+// memory pipeline for A_g alone.  UNI: a kv head's region of a block spans one
+// or more whole wave-loads (U >= 64), so the block of every load slot is the
+// same across the wave and its table entry and slab offset are scalar.
+// Off: 32-bit byte offsets when a layer's slab is below 4 GiB, else 64-bit.
+template <int LPR, int QH, int NS, bool QLDS, typename Off, bool UNI>
+__global__ __launch_bounds__(256)
+#if PRED_DECODE_WAVES_PER_EU
+__attribute__((amdgpu_waves_per_eu(PRED_DECODE_WAVES_PER_EU)))
+#endif
+void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
     extern __shared__ uint4 q_lds[];
     const int lane = threadIdx.x & 63;
+    const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t wgb = blockIdx.x % gm.wgs_per_seq;
     const int64_t ls = blockIdx.x / gm.wgs_per_seq;
     const int s = (int)(ls % a.S);
     const int l = (int)(ls / a.S);
-    const int64_t b_first = (wgb * kWaves + (threadIdx.x >> 6)) * gm.NBW;
+    const int64_t b_first = (wgb * kWaves + wave_id) * gm.NBW;
     const uint16_t* qrows = a.qp + ((int64_t)l * a.S + s) * (int64_t)a.M * a.Hq * a.R;
     if constexpr (QLDS) {
         const uint4* src = reinterpret_cast<const uint4*>(qrows);
@@ -131,27 +154,33 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a, DecodeGe
     const int64_t slot_elems = (int64_t)a.Hk * a.B * a.R;
 
     // Per load slot: byte offset, within this layer's A_g slab, of the lane's
-    // row of its block's region at kv head 0.  Slots past the end or with an
-    // invalid table entry read the slab's first row instead and are masked out
-    // of the max, so the loads need no branch.  With 32-bit offsets the loads
-    // take the uniform slab base from SGPRs and one VGPR per slot.
+    // row of its block's region at kv head 0.  The wave's NBW table entries
+    // (consecutive logical blocks) come in with one coalesced load, lane j
+    // holding block j, and each slot takes its block's entry from that lane.
+    // Slots past the end or with an invalid entry read the slab's first slot
+    // and are masked out of the max.
     const char* slab = reinterpret_cast<const char*>(a.ag + layer * a.N * slot_elems);
+    int32_t tab_lane = -1;
+    {
+        const int64_t b = b_first + lane;
+        if (lane < gm.NBW && b < a.n) tab_lane = a.tables ? a.tables[(int64_t)s * a.n + b] : (int32_t)b;
+    }
     Off voff[NS];
+    uint32_t soff_slot[NS];   // UNI: the whole slot offset is wave-uniform (SGPR)
     uint32_t live = 0;
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl) {
         const int f = sl * 64 + lane;
-        const int bi = f >> gm.log2U;
+        const int bi = UNI ? ((sl * 64) >> gm.log2U) : (f >> gm.log2U);
         const int t = (f & (gm.U - 1)) / LPR;
-        const int64_t b = b_first + bi;
-        voff[sl] = (Off)(p * 16);
-        if (bi < gm.NBW && b < a.n) {
-            const int64_t phys = a.tables ? (int64_t)a.tables[(int64_t)s * a.n + b] : b;
-            if (phys >= 0 && phys < a.N) {
-                voff[sl] = (Off)((phys * slot_elems + (int64_t)t * a.R + p * 8) * 2);
-                live |= 1u << sl;
-            }
-        }
+        int32_t phys;
+        if constexpr (UNI) phys = __builtin_amdgcn_readlane(tab_lane, bi);
+        else phys = __shfl(tab_lane, bi);
+        const bool ok = bi < gm.NBW && b_first + bi < a.n && phys >= 0 && (int64_t)phys < a.N;
+        voff[sl] = (Off)(((ok ? (int64_t)phys : 0) * slot_elems + (int64_t)t * a.R + p * 8) * 2);
+        // UNI: row t, lane part p of slot sl is byte 1024 * (sl % SPB) + 16 * lane of the block's region
+        soff_slot[sl] = (uint32_t)((ok ? (int64_t)phys : 0) * slot_elems * 2 + 1024 * (sl % gm.SPB));
+        live |= (ok ? 1u : 0u) << sl;
     }
 
     float rm[NS];
@@ -159,78 +188,109 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a, DecodeGe
     for (int sl = 0; sl < NS; ++sl) rm[sl] = -__builtin_inff();
 
     const int fx = label_xor<LPR, QH>(p);
-    const int64_t kv_stride = (int64_t)a.B * a.R;
+    const int64_t kv_bytes = (int64_t)a.B * a.R * 2;
+    // 32-bit offsets: raw buffer loads with the slab as the resource base, the
+    // lane offset in a VGPR and the kv-head offset in an SGPR.
+    __amdgpu_buffer_rsrc_t rsrc;
+    if constexpr (sizeof(Off) == 4)
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(slab), (short)0, (int)0xFFFFFFFF, 0x00020000);
     auto load_a = [&](uint4 (&dst)[NS], int kv) {
-        // dead slots read inside the slab's first slot
-        const char* kbase = slab + kv * kv_stride * 2;
+        if constexpr (sizeof(Off) == 4 && UNI) {
+            const uint32_t kvoff = (uint32_t)(kv * kv_bytes);
 #pragma unroll
-        for (int sl = 0; sl < NS; ++sl) dst[sl] = *reinterpret_cast<const uint4*>(kbase + voff[sl]);
+            for (int sl = 0; sl < NS; ++sl)
+                dst[sl] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        rsrc, lane * 16, (int)(soff_slot[sl] + kvoff), PRED_DECODE_AUX));
+        } else if constexpr (sizeof(Off) == 4) {
+            const int soff = (int)(kv * kv_bytes);
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl)
+                dst[sl] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)voff[sl], soff, PRED_DECODE_AUX));
+        } else {
+            const char* kbase = slab + kv * kv_bytes;
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl) dst[sl] = *reinterpret_cast<const uint4*>(kbase + voff[sl]);
+        }
     };
-
-    // A_g loads run one kv head ahead of the arithmetic.
-    uint4 av[NS], an[NS];
-    load_a(av, 0);
-    for (int hg = 0; hg < gm.n_groups; ++hg) {
-        for (int kv = 0; kv < a.Hk; ++kv) {
-            const bool more = (kv + 1 < a.Hk) || (hg + 1 < gm.n_groups);
-            if (more) load_a(an, kv + 1 < a.Hk ? kv + 1 : 0);
-            uint32_t q[QH][4];
+    auto score_kv = [&](const uint4 (&av)[NS], int kv, int hg) {
+        uint32_t q[QH][4];
+#pragma unroll
+        for (int i = 0; i < QH; ++i) {
+            int e = hg * QH + (i ^ fx);
+            if (e >= gm.n_eff) e = gm.n_eff - 1;  // padding: repeat a real head (max unchanged)
+            const int row = e / g;
+            const int h = e - row * g;
+            const int64_t off = ((int64_t)row * a.Hq + kv * g + h) * a.R + p * 8;
+            uint4 w;
+            if constexpr (QLDS) w = q_lds[off >> 3];
+            else w = *reinterpret_cast<const uint4*>(qrows + off);
+            q[i][0] = w.x; q[i][1] = w.y; q[i][2] = w.z; q[i][3] = w.w;
+        }
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+            float v[QH];
 #pragma unroll
             for (int i = 0; i < QH; ++i) {
-                int e = hg * QH + (i ^ fx);
-                if (e >= gm.n_eff) e = gm.n_eff - 1;  // padding: repeat a real head (max unchanged)
-                const int row = e / g;
-                const int h = e - row * g;
-                const int64_t off = ((int64_t)row * a.Hq + kv * g + h) * a.R + p * 8;
-                uint4 w;
-                if constexpr (QLDS) w = q_lds[off >> 3];
-                else w = *reinterpret_cast<const uint4*>(qrows + off);
-                q[i][0] = w.x; q[i][1] = w.y; q[i][2] = w.z; q[i][3] = w.w;
+                float acc = dot2(av[sl].x, q[i][0], 0.0f);
+                acc = dot2(av[sl].y, q[i][1], acc);
+                acc = dot2(av[sl].z, q[i][2], acc);
+                v[i] = dot2(av[sl].w, q[i][3], acc);
             }
+            reduce_levels<LPR, QH, 0>(v);
+            constexpr int rem = (QH / LPR) > 0 ? (QH / LPR) : 1;
+            float mx = v[0];
 #pragma unroll
-            for (int sl = 0; sl < NS; ++sl) {
-                float v[QH];
-#pragma unroll
-                for (int i = 0; i < QH; ++i) {
-                    float acc = dot2(av[sl].x, q[i][0], 0.0f);
-                    acc = dot2(av[sl].y, q[i][1], acc);
-                    acc = dot2(av[sl].z, q[i][2], acc);
-                    v[i] = dot2(av[sl].w, q[i][3], acc);
-                }
-                reduce_levels<LPR, QH, 0>(v);
-                constexpr int rem = (QH / LPR) > 0 ? (QH / LPR) : 1;
-                float mx = v[0];
-#pragma unroll
-                for (int i = 1; i < rem; ++i) mx = fmaxf(mx, v[i]);
-                rm[sl] = ((live >> sl) & 1u) ? fmaxf(rm[sl], mx) : rm[sl];
-            }
-            if (more) {
-#pragma unroll
-                for (int sl = 0; sl < NS; ++sl) av[sl] = an[sl];
-            }
+            for (int i = 1; i < rem; ++i) mx = fmaxf(mx, v[i]);
+            rm[sl] = ((live >> sl) & 1u) ? fmaxf(rm[sl], mx) : rm[sl];
+        }
+    };
+
+    // Two buffers in ping-pong: the loads of kv head k+1 are in flight while
+    // kv head k is scored.  The steady-state loop has no conditional loads, so
+    // each score step waits only for its own buffer.
+    uint4 A0[NS], A1[NS];
+    for (int hg = 0; hg < gm.n_groups; ++hg) {
+        load_a(A0, 0);
+        int kv = 0;
+        for (; kv + 2 < a.Hk; kv += 2) {
+            load_a(A1, kv + 1);
+            score_kv(A0, kv, hg);
+            load_a(A0, kv + 2);
+            score_kv(A1, kv + 1, hg);
+        }
+        if (kv + 1 < a.Hk) {
+            load_a(A1, kv + 1);
+            score_kv(A0, kv, hg);
+            score_kv(A1, kv + 1, hg);
+        } else {
+            score_kv(A0, kv, hg);
         }
     }
 
     // Block maxima and stores.
     float* out = a.scores + ((int64_t)l * a.S + s) * a.n;
-    if (gm.U >= 64) {
+    const int32_t* table = a.tables ? a.tables + (int64_t)s * a.n : nullptr;
+    auto store = [&](int bi, float v) {
+        const int64_t b = b_first + bi;
+        if (bi < gm.NBW && b < a.n) {
+            const int64_t phys = table ? (int64_t)table[b] : b;
+            if (phys >= 0 && phys < a.N) {
+                out[b] = v;
+            } else {
+                out[b] = __uint_as_float(0x7FC00000u);
+                atomicOr(a.err, DEVERR_TABLE);
+            }
+        }
+    };
+    if constexpr (UNI) {
         float acc = -__builtin_inff();
 #pragma unroll
         for (int sl = 0; sl < NS; ++sl) {
             acc = fmaxf(acc, rm[sl]);
             if ((sl + 1) % gm.SPB == 0) {
                 const float v = wave_max_xor(acc, 64);
-                const int bi = sl / gm.SPB;
-                const int64_t b = b_first + bi;
-                if (lane == 0 && bi < gm.NBW && b < a.n) {
-                    const int64_t phys = a.tables ? (int64_t)a.tables[(int64_t)s * a.n + b] : b;
-                    if (phys >= 0 && phys < a.N) {
-                        out[b] = v;
-                    } else {
-                        out[b] = __uint_as_float(0x7FC00000u);
-                        atomicOr(a.err, DEVERR_TABLE);
-                    }
-                }
+                if (lane == 0) store(sl / gm.SPB, v);
                 acc = -__builtin_inff();
             }
         }
@@ -239,17 +299,7 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a, DecodeGe
         for (int sl = 0; sl < NS; ++sl) {
             const float v = wave_max_xor(rm[sl], gm.U);
             const int f = sl * 64 + lane;
-            const int bi = f >> gm.log2U;
-            const int64_t b = b_first + bi;
-            if ((lane & (gm.U - 1)) == 0 && bi < gm.NBW && b < a.n) {
-                const int64_t phys = a.tables ? (int64_t)a.tables[(int64_t)s * a.n + b] : b;
-                if (phys >= 0 && phys < a.N) {
-                    out[b] = v;
-                } else {
-                    out[b] = __uint_as_float(0x7FC00000u);
-                    atomicOr(a.err, DEVERR_TABLE);
-                }
-            }
+            if ((lane & (gm.U - 1)) == 0) store(f >> gm.log2U, v);
         }
     }
 }
@@ -304,12 +354,15 @@ void launch_decode_t(const ScoreArgs& a, const DecodeGeom& gm, hipStream_t st) {
     const unsigned grid = (unsigned)(gm.wgs_per_seq * a.S * a.n_layers);
     const int q_bytes = gm.q_chunks * 16;
     const bool narrow = a.N * (int64_t)a.Hk * a.B * a.R * 2 < (int64_t(1) << 32);
-    if (q_bytes <= kQLdsMaxBytes && narrow)
-        score_decode_kernel<LPR, QH, NS, true, uint32_t><<<grid, 256, q_bytes, st>>>(a, gm);
-    else if (q_bytes <= kQLdsMaxBytes)
-        score_decode_kernel<LPR, QH, NS, true, uint64_t><<<grid, 256, q_bytes, st>>>(a, gm);
-    else
-        score_decode_kernel<LPR, QH, NS, false, uint64_t><<<grid, 256, 0, st>>>(a, gm);
+    const bool uni = gm.U >= 64;
+    if (q_bytes <= kQLdsMaxBytes && narrow) {
+        if (uni) score_decode_kernel<LPR, QH, NS, true, uint32_t, true><<<grid, 256, q_bytes, st>>>(a, gm);
+        else score_decode_kernel<LPR, QH, NS, true, uint32_t, false><<<grid, 256, q_bytes, st>>>(a, gm);
+    } else if (q_bytes <= kQLdsMaxBytes) {
+        score_decode_kernel<LPR, QH, NS, true, uint64_t, false><<<grid, 256, q_bytes, st>>>(a, gm);
+    } else {
+        score_decode_kernel<LPR, QH, NS, false, uint64_t, false><<<grid, 256, 0, st>>>(a, gm);
+    }
 }
 
 template <int LPR, int NS>
@@ -337,11 +390,11 @@ bool decode_geometry(const ScoreArgs& a, DecodeGeom& gm, int& ns, int& lpr, int&
     if (!(a.R == 16 || a.R == 32 || a.R == 64 || a.R == 128)) return false;
     lpr = a.R / 8;
     const int64_t U = (int64_t)a.B * lpr;
-    if (!is_pow2(U) || U > 1024) return false;
+    if (!is_pow2(U) || U > 1024 || U < 8) return false;
     gm.U = (int)U;
     gm.log2U = 0;
     while ((1 << gm.log2U) < gm.U) ++gm.log2U;
-    ns = (U >= 512) ? 16 : 8;
+    ns = (U >= 512 || PRED_DECODE_NS_SMALL == 16) ? 16 : 8;
     const int chunks = ns * 64;
     gm.NBW = (int)(chunks / U);
     gm.SPB = U >= 64 ? (int)(U / 64) : 1;
