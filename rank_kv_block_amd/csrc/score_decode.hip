@@ -35,6 +35,9 @@
 #ifndef PRED_DECODE_NS_SMALL
 #define PRED_DECODE_NS_SMALL 8
 #endif
+#ifndef PRED_DECODE_ROTATE
+#define PRED_DECODE_ROTATE 1
+#endif
 #ifndef PRED_DECODE_WAVES_PER_EU
 #define PRED_DECODE_WAVES_PER_EU 0
 #endif
@@ -142,12 +145,7 @@ void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
     const int l = (int)(ls / a.S);
     const int64_t b_first = (wgb * kWaves + wave_id) * gm.NBW;
     const uint16_t* qrows = a.qp + ((int64_t)l * a.S + s) * (int64_t)a.M * a.Hq * a.R;
-    if constexpr (QLDS) {
-        const uint4* src = reinterpret_cast<const uint4*>(qrows);
-        for (int i = threadIdx.x; i < gm.q_chunks; i += 256) q_lds[i] = src[i];
-        __syncthreads();
-    }
-    if (b_first >= a.n) return;   // after the only barrier
+    const bool has_work = b_first < a.n;   // wave-uniform; idle waves still meet the barrier
     const int p = lane & (LPR - 1);
     const int g = a.Hq / a.Hk;
     const int64_t layer = a.layer0 + l;
@@ -213,18 +211,29 @@ void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
             for (int sl = 0; sl < NS; ++sl) dst[sl] = *reinterpret_cast<const uint4*>(kbase + voff[sl]);
         }
     };
-    auto score_kv = [&](const uint4 (&av)[NS], int kv, int hg) {
-        uint32_t q[QH][4];
+    // Query fragment i of this lane at kv head 0, in 16-byte units: computed
+    // once per head group, the kv head only adds g*R/8 per step.
+    int qoff[QH];
+    auto set_qoff = [&](int hg) {
 #pragma unroll
         for (int i = 0; i < QH; ++i) {
             int e = hg * QH + (i ^ fx);
             if (e >= gm.n_eff) e = gm.n_eff - 1;  // padding: repeat a real head (max unchanged)
             const int row = e / g;
             const int h = e - row * g;
-            const int64_t off = ((int64_t)row * a.Hq + kv * g + h) * a.R + p * 8;
+            qoff[i] = (int)((((int64_t)row * a.Hq + h) * a.R + p * 8) >> 3);
+        }
+    };
+    const int q_kv_step = g * a.R / 8;
+    auto score_kv = [&](const uint4 (&av)[NS], int kv, int hg) {
+        (void)hg;
+        uint32_t q[QH][4];
+#pragma unroll
+        for (int i = 0; i < QH; ++i) {
+            const int o = qoff[i] + kv * q_kv_step;
             uint4 w;
-            if constexpr (QLDS) w = q_lds[off >> 3];
-            else w = *reinterpret_cast<const uint4*>(qrows + off);
+            if constexpr (QLDS) w = q_lds[o];
+            else w = reinterpret_cast<const uint4*>(qrows)[o];
             q[i][0] = w.x; q[i][1] = w.y; q[i][2] = w.z; q[i][3] = w.w;
         }
 #pragma unroll
@@ -248,23 +257,37 @@ void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
 
     // Two buffers in ping-pong: the loads of kv head k+1 are in flight while
     // kv head k is scored.  The steady-state loop has no conditional loads, so
-    // each score step waits only for its own buffer.
+    // each score step waits only for its own buffer.  The first buffer is
+    // requested before q_proj is staged in LDS, so both round trips overlap.
+    // Each wave starts at a different kv head (and wraps around), so the waves
+    // in flight spread their reads over every kv region's offset instead of
+    // all hitting offset k * B * R * 2 of their slots at the same time.
+    const int kv0 = PRED_DECODE_ROTATE ? (int)((b_first / gm.NBW) % a.Hk) : 0;
+    auto kvr = [&](int k) { const int r = kv0 + k; return r < a.Hk ? r : r - a.Hk; };
     uint4 A0[NS], A1[NS];
+    if (has_work) load_a(A0, kvr(0));
+    if constexpr (QLDS) {
+        const uint4* src = reinterpret_cast<const uint4*>(qrows);
+        for (int i = threadIdx.x; i < gm.q_chunks; i += 256) q_lds[i] = src[i];
+        __syncthreads();
+    }
+    if (!has_work) return;   // after the only barrier
     for (int hg = 0; hg < gm.n_groups; ++hg) {
-        load_a(A0, 0);
+        set_qoff(hg);
+        if (hg > 0) load_a(A0, kvr(0));
         int kv = 0;
         for (; kv + 2 < a.Hk; kv += 2) {
-            load_a(A1, kv + 1);
-            score_kv(A0, kv, hg);
-            load_a(A0, kv + 2);
-            score_kv(A1, kv + 1, hg);
+            load_a(A1, kvr(kv + 1));
+            score_kv(A0, kvr(kv), hg);
+            load_a(A0, kvr(kv + 2));
+            score_kv(A1, kvr(kv + 1), hg);
         }
         if (kv + 1 < a.Hk) {
-            load_a(A1, kv + 1);
-            score_kv(A0, kv, hg);
-            score_kv(A1, kv + 1, hg);
+            load_a(A1, kvr(kv + 1));
+            score_kv(A0, kvr(kv), hg);
+            score_kv(A1, kvr(kv + 1), hg);
         } else {
-            score_kv(A0, kv, hg);
+            score_kv(A0, kvr(kv), hg);
         }
     }
 
