@@ -4,16 +4,20 @@
 //
 // Scores map to order-preserving uint32 keys (-0 == +0, NaN first).  A segment
 // of up to 8192 keys is sorted inside one workgroup by an LSD radix sort over
-// eight 4-bit digits, keys and indices kept in LDS between passes.  Items sit
-// in blocked order (thread t owns positions t*IPT .. t*IPT+IPT-1), so a pass
-// is stable if each thread ranks its own items in order and the (digit,
-// thread) counts are scanned digit-major: the thread counts its items per
-// digit in a packed register (16 four-bit counters in 64 bits, IPT <= 15), with
-// no cross-lane work at all; one exclusive scan over the 16 x T counts in LDS
-// gives every (digit, thread) its first destination.  A pass whose digit is the
-// same for every item (common for the high digits of scores in a narrow range)
-// is the identity and is skipped.  The first pass starts in index order, so
-// equal keys end in index order.
+// eight 4-bit digits.  Items sit in blocked order (thread t owns positions
+// t*IPT .. t*IPT+IPT-1), so a pass is stable if each thread ranks its own items
+// in order and (digit, thread) counts are scanned digit-major:
+//   * a thread counts its items per digit in one packed register (sixteen
+//     4-bit counters in 64 bits, IPT <= 15) -- no cross-lane work;
+//   * the counts, as eight words of two 16-bit halves, are prefix-summed across
+//     the wave with DPP row shifts and row broadcasts, across the waves through
+//     one small LDS table, and across digits from the grand totals;
+//   * items are scattered as (key, index) pairs into one of two LDS buffers and
+//     read back in blocked order.
+// That is two barriers and about sixteen LDS instructions per thread and pass.
+// A pass whose digit is the same for every item (common for the high digits of
+// scores in a narrow range) is the identity and is skipped.  The first pass
+// starts in index order, so equal keys end in index order.
 //
 // Longer segments: sorted 8192-key runs of (key << 32 | index) go to the
 // workspace and are merged pairwise; each element finds its place in the
@@ -28,32 +32,57 @@ namespace {
 
 constexpr int kMaxLdsItems = 8192;
 
-__device__ inline uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(v, off);
-        if (lane >= off) v += o;
-    }
+template <int CTRL, int ROW_MASK>
+__device__ inline uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes (packed 16-bit halves add independently).
+__device__ inline uint32_t wave_incl_scan(uint32_t v) {
+    v += dpp<0x111, 0xF>(v);   // row_shr:1
+    v += dpp<0x112, 0xF>(v);   // row_shr:2
+    v += dpp<0x114, 0xF>(v);   // row_shr:4
+    v += dpp<0x118, 0xF>(v);   // row_shr:8
+    v += dpp<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
     return v;
 }
 
-// One workgroup per (segment, chunk) of up to CAP = 64*NW*IPT keys.
+// Inclusive prefix sum over lanes 0..15 (row 0); other rows get their own.
+__device__ inline uint32_t row_incl_scan(uint32_t v) {
+    v += dpp<0x111, 0xF>(v);
+    v += dpp<0x112, 0xF>(v);
+    v += dpp<0x114, 0xF>(v);
+    v += dpp<0x118, 0xF>(v);
+    return v;
+}
+
+__device__ inline uint32_t select8(const uint32_t (&o)[8], uint32_t i) {
+    const uint32_t a0 = (i & 1u) ? o[1] : o[0];
+    const uint32_t a1 = (i & 1u) ? o[3] : o[2];
+    const uint32_t a2 = (i & 1u) ? o[5] : o[4];
+    const uint32_t a3 = (i & 1u) ? o[7] : o[6];
+    const uint32_t b0 = (i & 2u) ? a1 : a0;
+    const uint32_t b1 = (i & 2u) ? a3 : a2;
+    return (i & 4u) ? b1 : b0;
+}
+
+// One workgroup per (segment, chunk) of up to CAP = 64*NW*IPT keys, NW <= 16.
 template <int NW, int IPT>
 __global__ __launch_bounds__(NW * 64) void rank_lds_kernel(const float* __restrict__ scores, int64_t n,
                                                            int64_t chunk_len, int nchunks,
                                                            int32_t* __restrict__ victims,
                                                            uint64_t* __restrict__ runs) {
-    static_assert(IPT <= 15 && IPT % 4 == 0, "packed 4-bit counters hold at most 15 items per thread");
+    static_assert(IPT <= 15 && IPT % 2 == 0, "packed 4-bit counters hold at most 15 items per thread");
+    static_assert(NW <= 16, "the cross-wave scan runs in one DPP row");
     constexpr int T = NW * 64;
     constexpr int CAP = T * IPT;
-    __shared__ __align__(16) uint32_t kbuf[CAP];
-    __shared__ __align__(16) uint32_t ibuf[CAP];
-    __shared__ __align__(16) uint16_t cnt[16 * T];   // [digit][thread]
-    __shared__ uint32_t wsum[NW];
+    __shared__ __align__(16) uint2 kvb[2][CAP];       // (key, index) pairs, double-buffered
+    __shared__ __align__(16) uint4 wsum[2][NW][2];    // per-wave digit totals, double-buffered
 
     const int t = threadIdx.x;
     const int lane = t & 63;
-    const int w = t >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t seg = blockIdx.x / nchunks;
     const int64_t off = (int64_t)(blockIdx.x % nchunks) * chunk_len;
     const int len = (int)((n - off) < chunk_len ? (n - off) : chunk_len);
@@ -72,8 +101,10 @@ __global__ __launch_bounds__(NW * 64) void rank_lds_kernel(const float* __restri
         }
     }
 
+    int buf = 0;
     for (int pass = 0; pass < 8; ++pass) {
         const int shift = 4 * pass;
+        const int wb = pass & 1;
         // rank each item among this thread's earlier items with the same digit
         uint64_t packed = 0;
         uint32_t dig[IPT], rnk[IPT];
@@ -84,63 +115,67 @@ __global__ __launch_bounds__(NW * 64) void rank_lds_kernel(const float* __restri
             rnk[j] = (uint32_t)(packed >> (4 * d)) & 15u;
             packed += 1ull << (4 * d);
         }
-#pragma unroll
-        for (int d = 0; d < 16; ++d) cnt[d * T + t] = (uint16_t)((packed >> (4 * d)) & 15u);
-        __syncthreads();
-        // exclusive scan of the 16*T counts in [digit][thread] order, 16 per thread
-        uint4* c4 = reinterpret_cast<uint4*>(cnt) + 2 * t;
-        const uint4 lo = c4[0], hi = c4[1];
-        const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        uint32_t vals[16];
-        uint32_t sum = 0;
+        // counts as eight words: word i = count(2i) | count(2i+1) << 16
+        uint32_t cnt[8], inc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            vals[2 * i] = wd[i] & 0xFFFFu;
-            vals[2 * i + 1] = wd[i] >> 16;
-            sum += vals[2 * i] + vals[2 * i + 1];
+            const uint32_t pair = (uint32_t)(packed >> (8 * i)) & 0xFFu;
+            cnt[i] = (pair & 15u) | ((pair >> 4) << 16);
+            inc[i] = wave_incl_scan(cnt[i]);
         }
-        const uint32_t incl = wave_incl_scan(sum, lane);
-        if (lane == 63) wsum[w] = incl;
+        if (lane == 63) {
+            wsum[wb][w][0] = make_uint4(inc[0], inc[1], inc[2], inc[3]);
+            wsum[wb][w][1] = make_uint4(inc[4], inc[5], inc[6], inc[7]);
+        }
         __syncthreads();
-        uint32_t run = incl - sum;
-        for (int ww = 0; ww < w; ++ww) run += wsum[ww];
-        uint32_t out[8];
+        // lanes 0..NW-1 scan the wave totals; every wave reads its prefix and the grand totals
+        uint4 t0 = make_uint4(0u, 0u, 0u, 0u), t1 = t0;
+        if (lane < NW) {
+            t0 = wsum[wb][lane][0];
+            t1 = wsum[wb][lane][1];
+        }
+        const uint32_t tw[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+        uint32_t base[8];
+        uint32_t grand[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const uint32_t a = run;
-            run += vals[2 * i];
-            const uint32_t b = run;
-            run += vals[2 * i + 1];
-            out[i] = a | (b << 16);
+            const uint32_t sc = row_incl_scan(tw[i]);
+            grand[i] = (uint32_t)__builtin_amdgcn_readlane((int)sc, NW - 1);
+            base[i] = w > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)sc, w - 1) : 0u;
         }
-        c4[0] = make_uint4(out[0], out[1], out[2], out[3]);
-        c4[1] = make_uint4(out[4], out[5], out[6], out[7]);
-        __syncthreads();
-        // a digit holding every item makes the pass the identity
-        uint32_t first = 0, next = CAP;
-        if (lane < 16) {
-            first = cnt[lane * T];
-            next = lane < 15 ? cnt[(lane + 1) * T] : (uint32_t)CAP;
+        // digit bases: exclusive prefix of the grand totals over digits 0..15
+        uint32_t run = 0;
+        bool identity = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t lo = grand[i] & 0xFFFFu, hi = grand[i] >> 16;
+            identity |= (lo == (uint32_t)CAP) | (hi == (uint32_t)CAP);
+            const uint32_t dlo = run;
+            const uint32_t dhi = run + lo;
+            run = dhi + hi;
+            base[i] += dlo | (dhi << 16);
         }
-        const bool identity = __ballot(lane < 16 && first == 0 && next == (uint32_t)CAP) != 0;
-        if (!identity) {   // uniform across the workgroup
+        if (identity) continue;   // uniform: one digit holds every item
+        // first destination of (digit, this thread)
+        uint32_t first[8];
 #pragma unroll
-            for (int j = 0; j < IPT; ++j) {
-                const uint32_t dst = cnt[dig[j] * T + t] + rnk[j];
-                kbuf[dst] = key[j];
-                ibuf[dst] = idx[j];
-            }
-            __syncthreads();
-            const uint4* k4 = reinterpret_cast<const uint4*>(kbuf) + t * (IPT / 4);
-            const uint4* i4 = reinterpret_cast<const uint4*>(ibuf) + t * (IPT / 4);
+        for (int i = 0; i < 8; ++i) first[i] = base[i] + inc[i] - cnt[i];
+        uint2* dstb = kvb[buf];
 #pragma unroll
-            for (int c = 0; c < IPT / 4; ++c) {
-                const uint4 kk = k4[c], ii = i4[c];
-                key[4 * c] = kk.x; key[4 * c + 1] = kk.y; key[4 * c + 2] = kk.z; key[4 * c + 3] = kk.w;
-                idx[4 * c] = ii.x; idx[4 * c + 1] = ii.y; idx[4 * c + 2] = ii.z; idx[4 * c + 3] = ii.w;
-            }
+        for (int j = 0; j < IPT; ++j) {
+            const uint32_t word = select8(first, dig[j] >> 1);
+            const uint32_t o = (dig[j] & 1u) ? (word >> 16) : (word & 0xFFFFu);
+            dstb[o + rnk[j]] = make_uint2(key[j], idx[j]);
         }
         __syncthreads();
+        const uint4* mine = reinterpret_cast<const uint4*>(dstb + t * IPT);
+#pragma unroll
+        for (int c = 0; c < IPT / 2; ++c) {
+            const uint4 v = mine[c];
+            key[2 * c] = v.x; idx[2 * c] = v.y;
+            key[2 * c + 1] = v.z; idx[2 * c + 1] = v.w;
+        }
+        buf ^= 1;
     }
 
 #pragma unroll

@@ -32,9 +32,6 @@
 #ifndef PRED_DECODE_AUX
 #define PRED_DECODE_AUX 2
 #endif
-#ifndef PRED_DECODE_NS_SMALL
-#define PRED_DECODE_NS_SMALL 8
-#endif
 #ifndef PRED_DECODE_ROTATE
 #define PRED_DECODE_ROTATE 1
 #endif
@@ -417,7 +414,16 @@ bool decode_geometry(const ScoreArgs& a, DecodeGeom& gm, int& ns, int& lpr, int&
     gm.U = (int)U;
     gm.log2U = 0;
     while ((1 << gm.log2U) < gm.U) ++gm.log2U;
-    ns = (U >= 512 || PRED_DECODE_NS_SMALL == 16) ? 16 : 8;
+    // 8 load slots per wave (two 8 KiB buffers in flight), or 4 when that
+    // would leave fewer than ~8 rounds of workgroups: smaller work items then
+    // shorten the drain at the end of the launch, which costs more than the
+    // shallower prefetch (measured on the 64 x 2048 and 32768-block shapes).
+    ns = U >= 512 ? 16 : 8;
+    if (ns == 8 && U <= 256) {
+        const int64_t nbw8 = 512 / U;
+        const int64_t wgs8 = ((a.n + nbw8 - 1) / nbw8 + kWaves - 1) / kWaves * a.S * a.n_layers;
+        if (wgs8 < 8192) ns = 4;
+    }
     const int chunks = ns * 64;
     gm.NBW = (int)(chunks / U);
     gm.SPB = U >= 64 ? (int)(U / 64) : 1;
@@ -438,6 +444,7 @@ hipError_t launch_score_decode_or_generic(const ScoreArgs& a, hipStream_t stream
     int ns, lpr, qh;
     if (decode_geometry(a, gm, ns, lpr, qh)) {
         if (ns == 16) launch_decode_ns<16>(a, gm, lpr, qh, stream);
+        else if (ns == 4) launch_decode_ns<4>(a, gm, lpr, qh, stream);
         else launch_decode_ns<8>(a, gm, lpr, qh, stream);
     } else {
         const int64_t total = (int64_t)a.n_layers * a.S * a.n;

@@ -120,6 +120,8 @@ SHAPES = [
     (1, 32, 8, 128, 64, 16, 64, 23, 1, 17, "perm"),        # 17 rows: many-row path
     (1, 12, 4, 64, 24, 16, 30, 30, 1, 1, "perm"),          # r = 24: plain per-block kernel
     (1, 8, 2, 32, 16, 12, 60, 29, 2, 1, "identity"),       # block_size 12: plain per-block kernel
+    (1, 16, 2, 64, 128, 32, 40, 37, 1, 1, "perm"),         # 1 KiB-wide kv regions: 16 load slots per wave
+    (2, 32, 8, 128, 32, 16, 9000, 8200, 1, 1, "perm"),     # larger ragged case, two layers
     # many query rows: the MFMA scorer
     (1, 32, 8, 128, 64, 16, 300, 260, 1, 64, "perm"),      # prefill-chunk dims, ragged key tiles
     (2, 16, 4, 64, 32, 32, 150, 70, 2, 40, "perm"),        # block_size 32, two layers, two sequences
