@@ -22,7 +22,12 @@ COMMON = [
 ]
 SOURCES = ["pred_api.hip", "proj.hip", "score_decode.hip", "score_prefill.hip", "rank.hip", "prng.cpp"]
 # the projection generator must be plain IEEE float64 arithmetic, one operation at a time
-EXTRA = {"prng.cpp": ["-ffp-contract=off", "-fno-fast-math"]}
+EXTRA = {
+    "prng.cpp": ["-ffp-contract=off", "-fno-fast-math"],
+    # MFMA results straight into VGPRs: the max epilogue then reads them without
+    # accumulator-register copies
+    "score_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src):

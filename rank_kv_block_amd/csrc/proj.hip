@@ -146,29 +146,32 @@ __global__ __launch_bounds__(256) void project_mfma_kernel(const uint16_t* __res
     const int q = lane >> 4;
     const int j = jt * 16 + col;
 
-    double pb[DG];   // B operands: P[q*DG + s][j]
-#pragma unroll
-    for (int s = 0; s < DG; ++s) pb[s] = pf[(int64_t)(q * DG + s) * R + j];
-
     const int64_t v_first = vgrp * VT * 16;
     if (v_first >= n_vec) return;
     const int64_t v_end = (v_first + (int64_t)VT * 16) < n_vec ? (v_first + (int64_t)VT * 16) : n_vec;
     auto clamp_row = [&](int64_t r) { return r < n_vec ? r : n_vec - 1; };  // tail rows are computed, not stored
 
+    // the first input tile and this wave's slice of P are requested together
     uint4 w[DG / 8], wn[DG / 8];
     load_row_quarter<DG>(in, clamp_row(v_first + col), q, w);
+    double pb[DG];   // B operands: P[q*DG + s][j]
+#pragma unroll
+    for (int s = 0; s < DG; ++s) pb[s] = pf[(int64_t)(q * DG + s) * R + j];
+
     for (int64_t v0 = v_first; v0 < v_end; v0 += 16) {
         if (v0 + 16 < v_end) load_row_quarter<DG>(in, clamp_row(v0 + 16 + col), q, wn);
-        f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+        // two accumulators (even / odd k-steps) halve the dependent MFMA chain
+        f64x4_t acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
         for (int c = 0; c < DG / 8; ++c) {
             const uint32_t ww[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_lo(ww[e]), pb[c * 8 + 2 * e], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_hi(ww[e]), pb[c * 8 + 2 * e + 1], acc, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_lo(ww[e]), pb[c * 8 + 2 * e], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_hi(ww[e]), pb[c * 8 + 2 * e + 1], acc1, 0, 0, 0);
             }
         }
+        const f64x4_t acc = acc0 + acc1;
         // acc[v] of lane group q is output (row v0 + q + 4v, column j)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {

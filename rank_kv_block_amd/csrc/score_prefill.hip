@@ -116,14 +116,21 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, Prefill
         const uint16_t* qnext = q_src(qt + 1 < gm.q_tiles ? qt + 1 : qt);
 #pragma unroll
         for (int st = 0; st < RS; ++st) qn[st] = load8(qnext + st * 16);
+        // all key tiles' MFMAs first, each into its own accumulator, so the
+        // max epilogue of one tile overlaps the matrix work of the next
+        f32x16_t acc[NKT];
 #pragma unroll
         for (int t = 0; t < NKT; ++t) {
-            f32x16_t acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0], kb[t][0], f32x16_t{}, 0, 0, 0);
 #pragma unroll
-            for (int st = 0; st < RS; ++st) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], kb[t][st], acc, 0, 0, 0);
-            float m = fmaxf(acc[0], acc[1]);
+            for (int st = 1; st < RS; ++st)
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], kb[t][st], acc[t], 0, 0, 0);
+        }
 #pragma unroll
-            for (int i = 2; i < 16; ++i) m = fmaxf(m, acc[i]);
+        for (int t = 0; t < NKT; ++t) {
+            float m = fmaxf(acc[t][0], acc[t][1]);
+#pragma unroll
+            for (int i = 2; i < 16; ++i) m = fmaxf(m, acc[t][i]);
             rm[t] = fmaxf(rm[t], m);
         }
 #pragma unroll
