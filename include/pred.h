@@ -160,8 +160,9 @@ int pred_score_blocks(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf
 int pred_rank_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments,
                       int32_t* victims, void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace pred_rank_victims needs for this shape (0 when every segment is
- * sorted inside one workgroup). */
+/* Workspace pred_rank_victims needs for this shape: 0 for n_blocks <= 2048
+ * (each segment is sorted inside one workgroup), else 8 bytes per key for the
+ * sorted runs, twice that for n_blocks > 8192 (pairwise merge buffers). */
 size_t pred_rank_workspace_bytes(int64_t n_blocks, int64_t n_segments);
 
 /* ------------------------------------------------------------------ inspection */

@@ -19,10 +19,20 @@
 // scores in a narrow range) is the identity and is skipped.  The first pass
 // starts in index order, so equal keys end in index order.
 //
-// Longer segments: sorted 8192-key runs of (key << 32 | index) go to the
-// workspace and are merged pairwise; each element finds its place in the
-// merged run by binary search in the other run (the 64-bit composites are
-// distinct, so positions never collide).
+// Segments over 2048 keys use every CU instead of one per segment:
+//   1. chunks of 1024 keys are sorted as above, one workgroup each, and written
+//      as sorted runs of keys and of their indexes;
+//   2. runs are merged in groups of up to 8192 keys by counting: one workgroup
+//      per run loads its group's keys into LDS, and each element's place in the
+//      group is its index in its own run plus, for every other run, how many of
+//      that run's keys come before it -- keys below it, and for a run of lower
+//      indexes (an earlier chunk) also keys equal to it.  A branch-free binary
+//      search over the run (padded to 1024 with keys above every real one)
+//      counts them;
+//   3. groups (segments over 8192 keys) are merged pairwise as 64-bit
+//      (key << 32 | index) composites, which are distinct and order exactly as
+//      the stable sort must; each element finds its place in the merged run by
+//      binary search in the other run.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,7 +40,20 @@ namespace pred {
 
 namespace {
 
-constexpr int kMaxLdsItems = 8192;
+constexpr int kMaxLdsItems = 8192;   // keys one workgroup sorts or merges in LDS
+constexpr int kChunk = 1024;         // keys per sorted run of step 1
+constexpr int kSingle = 2048;        // up to this many keys a segment is sorted by one workgroup
+
+// step 1 workgroup shape for a chunk (waves x keys per thread = kChunk / 64) and
+// step 2 threads per workgroup
+#ifndef PRED_RANK_NW
+#define PRED_RANK_NW 4
+#define PRED_RANK_IPT 4
+#endif
+#ifndef PRED_RANK_MERGE_TPB
+#define PRED_RANK_MERGE_TPB 1024
+#endif
+static_assert(PRED_RANK_NW * 64 * PRED_RANK_IPT == kChunk, "a step-1 workgroup sorts one chunk");
 
 template <int CTRL, int ROW_MASK>
 __device__ inline uint32_t dpp(uint32_t v) {
@@ -57,11 +80,21 @@ __device__ inline uint32_t row_incl_scan(uint32_t v) {
     return v;
 }
 
+// o[i] for a per-lane i in 0..7, as a tree of selects on registers.  The
+// words are made opaque first: otherwise the compiler turns the selects back
+// into an indexed array and places it in LDS (or scratch), costing a round trip
+// per item.
 __device__ inline uint32_t select8(const uint32_t (&o)[8], uint32_t i) {
-    const uint32_t a0 = (i & 1u) ? o[1] : o[0];
-    const uint32_t a1 = (i & 1u) ? o[3] : o[2];
-    const uint32_t a2 = (i & 1u) ? o[5] : o[4];
-    const uint32_t a3 = (i & 1u) ? o[7] : o[6];
+    uint32_t r[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        r[k] = o[k];
+        asm volatile("" : "+v"(r[k]));
+    }
+    const uint32_t a0 = (i & 1u) ? r[1] : r[0];
+    const uint32_t a1 = (i & 1u) ? r[3] : r[2];
+    const uint32_t a2 = (i & 1u) ? r[5] : r[4];
+    const uint32_t a3 = (i & 1u) ? r[7] : r[6];
     const uint32_t b0 = (i & 2u) ? a1 : a0;
     const uint32_t b1 = (i & 2u) ? a3 : a2;
     return (i & 4u) ? b1 : b0;
@@ -72,7 +105,8 @@ template <int NW, int IPT>
 __global__ __launch_bounds__(NW * 64) void rank_lds_kernel(const float* __restrict__ scores, int64_t n,
                                                            int64_t chunk_len, int nchunks,
                                                            int32_t* __restrict__ victims,
-                                                           uint64_t* __restrict__ runs) {
+                                                           uint32_t* __restrict__ run_keys,
+                                                           uint32_t* __restrict__ run_idx) {
     static_assert(IPT <= 15 && IPT % 2 == 0, "packed 4-bit counters hold at most 15 items per thread");
     static_assert(NW <= 16, "the cross-wave scan runs in one DPP row");
     constexpr int T = NW * 64;
@@ -182,8 +216,97 @@ __global__ __launch_bounds__(NW * 64) void rank_lds_kernel(const float* __restri
     for (int j = 0; j < IPT; ++j) {
         const int pos = t * IPT + j;
         if (pos < len) {
-            if (runs) runs[seg * n + off + pos] = ((uint64_t)key[j] << 32) | idx[j];
-            else victims[seg * n + off + pos] = (int32_t)idx[j];
+            if (run_keys) {
+                run_keys[seg * n + off + pos] = key[j];
+                run_idx[seg * n + off + pos] = idx[j];
+            } else {
+                victims[seg * n + off + pos] = (int32_t)idx[j];
+            }
+        }
+    }
+}
+
+// Step 2: one workgroup per (segment, run).  Runs of kChunk keys, grouped by
+// group_len (a multiple of kChunk, at most kMaxLdsItems); the output is the group
+// sorted, as victims when one group spans the segment, else as composites.
+template <int TPB>
+__global__ __launch_bounds__(TPB) void rank_count_merge_kernel(const uint32_t* __restrict__ run_keys,
+                                                               const uint32_t* __restrict__ run_idx, int64_t n,
+                                                               int64_t group_len, int nruns,
+                                                               int32_t* __restrict__ victims,
+                                                               uint64_t* __restrict__ out) {
+    constexpr int G = kMaxLdsItems / kChunk;   // runs per group, at most
+    constexpr int E = kChunk / TPB;            // elements of the run per thread
+    constexpr int L = kMaxLdsItems / TPB;      // group keys loaded per thread
+    __shared__ uint32_t gk[kMaxLdsItems];
+    const int t = threadIdx.x;
+    const int64_t seg = blockIdx.x / nruns;
+    const int run = (int)(blockIdx.x % nruns);
+    const int64_t run0 = (int64_t)run * kChunk;                       // run start in the segment
+    const int64_t g0 = (run0 / group_len) * group_len;                // group start
+    const int glen = (int)((n - g0) < group_len ? (n - g0) : group_len);
+    const int own = (int)((run0 - g0) / kChunk);
+    const uint32_t* src = run_keys + seg * n + g0;
+    {
+        // the group's keys, padded to G full runs with a key above every real one
+        // (order keys never exceed that of +inf); clamped indexes keep every load
+        // in bounds and let all of them issue back to back
+        uint32_t v[L];
+#pragma unroll
+        for (int k = 0; k < L; ++k) {
+            const int i = t + TPB * k;
+            v[k] = src[i < glen ? i : glen - 1];
+        }
+#pragma unroll
+        for (int k = 0; k < L; ++k) {
+            const int i = t + TPB * k;
+            gk[i] = i < glen ? v[k] : 0xFFFFFFFFu;
+        }
+    }
+    __syncthreads();
+
+    const int rlen = (glen - own * kChunk) < kChunk ? (glen - own * kChunk) : kChunk;
+    uint32_t x[E];
+    int pos[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = t + TPB * e;
+        x[e] = gk[own * kChunk + (i < rlen ? i : 0)];
+        pos[e] = i;   // the elements of its own run before it
+    }
+    // every run is searched (the own run too, its count discarded): no branch, so
+    // the G * E searches are independent chains of LDS reads that interleave
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+        const uint32_t bias = r < own ? 1u : 0u;   // earlier run: equal keys count as well
+        const uint32_t* a = gk + r * kChunk;
+        uint32_t xr[E];
+        int lo[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            xr[e] = x[e] + bias;                   // no overflow: x <= order key of +inf
+            lo[e] = 0;
+        }
+#pragma unroll
+        for (int step = kChunk / 2; step >= 1; step >>= 1) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) lo[e] += a[lo[e] + step - 1] < xr[e] ? step : 0;
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            lo[e] += a[lo[e]] < xr[e] ? 1 : 0;     // lo <= kChunk - 1 before this
+            pos[e] += r == own ? 0 : lo[e];
+        }
+    }
+    const bool whole = g0 == 0 && glen == n;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = t + TPB * e;
+        if (i < rlen && pos[e] < glen) {   // pos < glen always holds; never write outside the group
+            const int64_t dst = seg * n + g0 + pos[e];
+            const uint32_t id = run_idx[seg * n + run0 + i];
+            if (whole) victims[dst] = (int32_t)id;
+            else out[dst] = ((uint64_t)x[e] << 32) | id;
         }
     }
 }
@@ -221,44 +344,57 @@ __global__ __launch_bounds__(256) void rank_merge_kernel(const uint64_t* __restr
 
 template <int NW, int IPT>
 void launch_lds(const float* scores, int64_t n, int64_t chunk_len, int nchunks, int64_t n_seg,
-                int32_t* victims, uint64_t* runs, hipStream_t st) {
+                int32_t* victims, uint32_t* run_keys, uint32_t* run_idx, hipStream_t st) {
     rank_lds_kernel<NW, IPT><<<(unsigned)(n_seg * nchunks), NW * 64, 0, st>>>(scores, n, chunk_len, nchunks,
-                                                                              victims, runs);
+                                                                              victims, run_keys, run_idx);
 }
 
 }  // namespace
 
 size_t rank_workspace_bytes(int64_t n, int64_t n_seg) {
-    if (n <= kMaxLdsItems || n_seg <= 0) return 0;
-    return (size_t)(2 * n * n_seg) * sizeof(uint64_t);
+    if (n <= kSingle || n_seg <= 0) return 0;
+    // sorted runs; segments over kMaxLdsItems keys also need a second buffer for the pairwise merges
+    return (size_t)((n <= kMaxLdsItems ? 1 : 2) * n * n_seg) * sizeof(uint64_t);
 }
 
 hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int32_t* victims, void* ws,
                        hipStream_t st) {
     if (n <= 0 || n_seg <= 0) return hipSuccess;
     if (n <= 512) {
-        launch_lds<1, 8>(scores, n, n, 1, n_seg, victims, nullptr, st);
-    } else if (n <= 2048) {
-        launch_lds<4, 8>(scores, n, n, 1, n_seg, victims, nullptr, st);
-    } else if (n <= kMaxLdsItems) {
-        launch_lds<16, 8>(scores, n, n, 1, n_seg, victims, nullptr, st);
-    } else {
-        uint64_t* r0 = static_cast<uint64_t*>(ws);
-        uint64_t* r1 = r0 + n * n_seg;
-        const int nchunks = (int)((n + kMaxLdsItems - 1) / kMaxLdsItems);
-        launch_lds<16, 8>(scores, n, kMaxLdsItems, nchunks, n_seg, nullptr, r0, st);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        const unsigned grid = (unsigned)((n * n_seg + 255) / 256);
-        for (int64_t run = kMaxLdsItems; run < n; run *= 2) {
-            const bool last = 2 * run >= n;
-            rank_merge_kernel<<<grid, 256, 0, st>>>(r0, r1, last ? victims : nullptr, n, n_seg, run);
-            e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            uint64_t* tmp = r0; r0 = r1; r1 = tmp;
-        }
+        launch_lds<1, 8>(scores, n, n, 1, n_seg, victims, nullptr, nullptr, st);
+        return hipGetLastError();
     }
-    return hipGetLastError();
+    if (n <= kSingle) {
+        launch_lds<4, 8>(scores, n, n, 1, n_seg, victims, nullptr, nullptr, st);
+        return hipGetLastError();
+    }
+    // workspace: run keys and run indexes (4 + 4 bytes per key), then for long
+    // segments one more 8 bytes per key for the pairwise merges
+    uint32_t* rk = static_cast<uint32_t*>(ws);
+    uint32_t* ri = rk + n * n_seg;
+    uint64_t* r0 = static_cast<uint64_t*>(ws);
+    uint64_t* r1 = r0 + n * n_seg;
+    const int nruns = (int)((n + kChunk - 1) / kChunk);
+    launch_lds<PRED_RANK_NW, PRED_RANK_IPT>(scores, n, kChunk, nruns, n_seg, nullptr, rk, ri, st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t group = n < kMaxLdsItems ? n : kMaxLdsItems;
+    rank_count_merge_kernel<PRED_RANK_MERGE_TPB><<<(unsigned)(n_seg * nruns), PRED_RANK_MERGE_TPB, 0, st>>>(
+        rk, ri, n, group, nruns, victims, n <= kMaxLdsItems ? nullptr : r1);
+    e = hipGetLastError();
+    if (e != hipSuccess || n <= kMaxLdsItems) return e;
+    // sorted groups of kMaxLdsItems are in r1; merge them pairwise
+    uint64_t* in = r1;
+    uint64_t* outb = r0;
+    const unsigned grid = (unsigned)((n * n_seg + 255) / 256);
+    for (int64_t run = kMaxLdsItems; run < n; run *= 2) {
+        const bool last = 2 * run >= n;
+        rank_merge_kernel<<<grid, 256, 0, st>>>(in, outb, last ? victims : nullptr, n, n_seg, run);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        uint64_t* tmp = in; in = outb; outb = tmp;
+    }
+    return hipSuccess;
 }
 
 }  // namespace pred

@@ -102,7 +102,9 @@ def test_null_handle_errors():
 
 
 def test_rank_workspace_sizes():
-    assert rk.pred_rank_workspace_bytes(8192, 32) == 0
+    assert rk.pred_rank_workspace_bytes(2048, 32) == 0
+    assert rk.pred_rank_workspace_bytes(2049, 2) == 2049 * 2 * 8
+    assert rk.pred_rank_workspace_bytes(8192, 32) == 8192 * 32 * 8
     assert rk.pred_rank_workspace_bytes(8193, 1) == 2 * 8193 * 8
     assert rk.pred_rank_workspace_bytes(32768, 1) == 2 * 32768 * 8
     assert rk.pred_rank_workspace_bytes(20000, 3) == 2 * 20000 * 3 * 8

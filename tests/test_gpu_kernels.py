@@ -177,7 +177,9 @@ def test_random_shape_parity(shape):
 
 # ---------------------------------------------------------------- ranking
 
-@pytest.mark.parametrize("n,segs", [(1, 1), (5, 3), (64, 1), (513, 2), (2048, 4), (8192, 2), (8193, 1),
+@pytest.mark.parametrize("n,segs", [(1, 1), (5, 3), (64, 1), (513, 2), (1024, 3), (1025, 2), (2048, 4), (2049, 3),
+                                    (3000, 5), (4095, 2),
+                                    (8191, 1), (8192, 2), (8193, 1),
                                     (16384, 1), (16385, 1), (24576, 3), (40000, 2), (65536, 1)])
 def test_rank_exact(n, segs):
     _say("rank", n, segs)
@@ -215,7 +217,8 @@ def test_rank_special_orders(kind):
     d = rk.dims(1, 1, 1, 8, 8, 1, 1)
     with rk.Predictor(d, 1) as p:
         vic = torch.empty((2, n), dtype=torch.int32, device="cuda")
-        rk.pred_rank_victims(p.handle, torch.from_numpy(s).cuda(), vic)
+        ws = torch.empty((rk.pred_rank_workspace_bytes(n, 2) // 8,), dtype=torch.int64, device="cuda")
+        rk.pred_rank_victims(p.handle, torch.from_numpy(s).cuda(), vic, ws)
         got = vic.cpu().numpy()
     assert np.array_equal(got, predictor.rank_victims(s))
 
@@ -223,11 +226,12 @@ def test_rank_special_orders(kind):
 def test_rank_requires_workspace():
     d = rk.dims(1, 1, 1, 8, 8, 1, 1)
     with rk.Predictor(d, 1) as p:
-        sc = torch.zeros((1, 20000), dtype=torch.float32, device="cuda")
-        vic = torch.empty((1, 20000), dtype=torch.int32, device="cuda")
-        with pytest.raises(rk.PredError) as e:
-            rk.pred_rank_victims(p.handle, sc, vic, None)
-        assert e.value.code == rk.PRED_ERR_WORKSPACE
+        for n in (2049, 20000):
+            sc = torch.zeros((1, n), dtype=torch.float32, device="cuda")
+            vic = torch.empty((1, n), dtype=torch.int32, device="cuda")
+            with pytest.raises(rk.PredError) as e:
+                rk.pred_rank_victims(p.handle, sc, vic, None)
+            assert e.value.code == rk.PRED_ERR_WORKSPACE
 
 
 # ---------------------------------------------------------------- error paths
