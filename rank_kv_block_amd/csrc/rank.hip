@@ -41,7 +41,10 @@ namespace pred {
 namespace {
 
 constexpr int kMaxLdsItems = 8192;   // keys one workgroup sorts or merges in LDS
-constexpr int kChunk = 1024;         // keys per sorted run of step 1
+#ifndef PRED_RANK_CHUNK
+#define PRED_RANK_CHUNK 1024
+#endif
+constexpr int kChunk = PRED_RANK_CHUNK;   // keys per sorted run of step 1
 constexpr int kSingle = 2048;        // up to this many keys a segment is sorted by one workgroup
 
 // step 1 workgroup shape for a chunk (waves x keys per thread = kChunk / 64) and
@@ -54,6 +57,7 @@ constexpr int kSingle = 2048;        // up to this many keys a segment is sorted
 #define PRED_RANK_MERGE_TPB 1024
 #endif
 static_assert(PRED_RANK_NW * 64 * PRED_RANK_IPT == kChunk, "a step-1 workgroup sorts one chunk");
+static_assert(PRED_RANK_MERGE_TPB <= kChunk, "a step-2 thread places at least one key of its run");
 
 template <int CTRL, int ROW_MASK>
 __device__ inline uint32_t dpp(uint32_t v) {
