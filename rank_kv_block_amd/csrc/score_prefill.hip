@@ -7,17 +7,20 @@
 // f32 accumulation) with the max fused into the epilogue, so the [M*g, n*B]
 // product never leaves registers.
 //
-// Tiling: a workgroup owns one (layer, sequence, kv head) and 4 waves x NKT key
-// tiles of 32 keys (consecutive tokens of consecutive blocks).  A wave keeps its
-// keys as MFMA B operands in registers for the whole kernel and streams every
-// 32-query tile of its kv head as the A operand (the queries of one kv head are
-// at most a few MiB and stay in L2).  Each lane of the 32x32 f32 accumulator
-// holds one key column; the lane keeps a running max of its column over all
-// query tiles.  At the end the two lane halves are combined, then the 16 (or 8,
-// 32) lanes of one block, and the block's max goes to the score array with an
-// atomic max on an order-preserving uint32 key (kv heads sit in different
-// workgroups).  A fill kernel clears the keys first and a last kernel turns
-// them back into float32 in place.
+// Tiling: a workgroup owns one (layer, sequence, kv head, query part) and 4
+// waves x NKT key tiles of 32 keys (consecutive tokens of consecutive blocks).
+// A wave keeps its keys as MFMA B operands in registers for the whole kernel.
+// The part's queries stream through LDS in chunks of kChunk: the 256 threads
+// load a chunk with coalesced 16-byte reads while the previous chunk is being
+// multiplied, and every wave reads its A operands from LDS in the MFMA layout
+// (rows padded by 16 bytes so one read's rows fall in distinct banks).  Each
+// lane of the 32x32 f32 accumulator holds one key column (16 of the tile's 32
+// query rows); the lane keeps a running max of its column over all query
+// tiles.  At the end the two lane halves are combined, then the 8, 16 or 32
+// lanes of one block, and the block's max goes to the score array with an
+// atomic max on an order-preserving uint32 key (kv heads and query parts sit in
+// different workgroups).  A fill kernel clears the keys first and a last kernel
+// turns them back into float32 in place.
 //
 // Workgroups are numbered kv-head fastest, so with 8 kv heads each XCD (which
 // takes every 8th workgroup) serves one kv head and its L2 holds one kv head's
@@ -33,10 +36,16 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = 4;
+#ifndef PRED_PREFILL_CHUNK
+#define PRED_PREFILL_CHUNK 64
+#endif
+constexpr int kChunk = PRED_PREFILL_CHUNK;   // queries per LDS stage (a multiple of 32)
 
 struct PrefillGeom {
     int n_eff;            // queries per kv head = M * g
-    int q_tiles;          // ceil(n_eff / 32)
+    int chunks;           // ceil(n_eff / kChunk)
+    int q_split;          // query parts (workgroups per key group and kv head)
+    int chunks_per_part;
     int64_t n_keys;       // n * B keys per sequence
     int64_t groups;       // key groups per (layer, sequence, kv head)
 };
@@ -54,25 +63,39 @@ __device__ inline bf16x8_t load8(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
 }
 
-template <int RS, int NKT, int BS>
+// R: projected width; NKT: 32-key tiles per wave; BS: block size in tokens.
+template <int R, int NKT, int BS>
 __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, PrefillGeom gm, uint32_t* __restrict__ keys) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    constexpr int RS = R / 16;                  // MFMA k-steps of 16
+    constexpr int CPR = R / 8;                  // 16-byte pieces per query vector
+    constexpr int ROWB = R * 2 + 16;            // LDS bytes per query row (16 bytes of padding)
+    constexpr int PIECES = kChunk * CPR;        // 16-byte pieces per chunk
+    constexpr int PPT = (PIECES + 255) / 256;   // pieces per thread
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2][kChunk * ROWB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int kv = (int)(blockIdx.x % a.Hk);
     int64_t rest = blockIdx.x / a.Hk;
+    const int part = (int)(rest % gm.q_split);
+    rest /= gm.q_split;
     const int64_t grp = rest % gm.groups;
     rest /= gm.groups;
     const int s = (int)(rest % a.S);
     const int l = (int)(rest / a.S);
+    const int c_begin = part * gm.chunks_per_part;
+    const int c_end = (c_begin + gm.chunks_per_part) < gm.chunks ? (c_begin + gm.chunks_per_part) : gm.chunks;
+    if (c_begin >= c_end) return;   // whole workgroup: no query in this part
     const int g = a.Hq / a.Hk;
-    const int col = lane & 31;
-    const int half = lane >> 5;
+    const int col = lane & 31;      // key column of a tile / query row of a tile
+    const int half = lane >> 5;     // which 8 of the 16 k-values of one MFMA step
     const int64_t key0 = (grp * kWaves + wave) * (NKT * 32);
-    if (key0 >= gm.n_keys) return;   // whole wave past the end (no barriers in this kernel)
+    const bool active = key0 < gm.n_keys;   // wave-uniform; idle waves still take part in the barriers
     const int64_t layer = a.layer0 + l;
-    const int64_t slot_elems = (int64_t)a.Hk * BS * a.R;
+    const int64_t slot_elems = (int64_t)a.Hk * BS * R;
 
-    // B operands: this lane's key column of every key tile, R/16 k-steps of 8 values.
+    // B operands: this lane's key column of every key tile, k-values st*16 + half*8 .. +8.
     bf16x8_t kb[NKT][RS];
     uint32_t live = 0;
 #pragma unroll
@@ -84,7 +107,7 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, Prefill
             const int tok = (int)(key - b * BS);
             const int64_t phys = a.tables ? (int64_t)a.tables[(int64_t)s * a.n + b] : b;
             if (phys >= 0 && phys < a.N) {
-                src = a.ag + (layer * a.N + phys) * slot_elems + ((int64_t)kv * BS + tok) * a.R;
+                src = a.ag + (layer * a.N + phys) * slot_elems + ((int64_t)kv * BS + tok) * R;
                 live |= 1u << t;
             }
         }
@@ -96,26 +119,37 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, Prefill
 #pragma unroll
     for (int t = 0; t < NKT; ++t) rm[t] = -__builtin_inff();
 
-    const uint16_t* qrows = a.qp + ((int64_t)l * a.S + s) * (int64_t)a.M * a.Hq * a.R;
-    auto q_src = [&](int qt) {
-        int e = qt * 32 + col;
-        if (e >= gm.n_eff) e = gm.n_eff - 1;   // padding rows repeat a real query
-        const int row = e / g;
-        const int h = e - row * g;
-        return qrows + ((int64_t)row * a.Hq + kv * g + h) * a.R + half * 8;
+    // query chunk c -> registers (16-byte piece p: query row p / CPR, piece p % CPR)
+    const uint16_t* qrows = a.qp + ((int64_t)l * a.S + s) * (int64_t)a.M * a.Hq * R;
+    uint4 gq[PPT];
+    auto load_chunk = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int p = tid + 256 * i;
+            if (PIECES % 256 == 0 || p < PIECES) {
+                int e = c * kChunk + p / CPR;
+                if (e >= gm.n_eff) e = gm.n_eff - 1;   // padding rows repeat a real query
+                const int row = e / g;
+                const int h = e - row * g;
+                gq[i] = *reinterpret_cast<const uint4*>(qrows + ((int64_t)row * a.Hq + kv * g + h) * R + (p % CPR) * 8);
+            }
+        }
     };
-    // A operands of the current query tile; the next tile's are loaded before
-    // the current tile's MFMAs so the load latency hides behind them.
-    bf16x8_t qa[RS], qn[RS];
-    {
-        const uint16_t* q0 = q_src(0);
+    auto store_chunk = [&](int buf) {
 #pragma unroll
-        for (int st = 0; st < RS; ++st) qa[st] = load8(q0 + st * 16);
-    }
-    for (int qt = 0; qt < gm.q_tiles; ++qt) {
-        const uint16_t* qnext = q_src(qt + 1 < gm.q_tiles ? qt + 1 : qt);
+        for (int i = 0; i < PPT; ++i) {
+            const int p = tid + 256 * i;
+            if (PIECES % 256 == 0 || p < PIECES)
+                *reinterpret_cast<uint4*>(&lds[buf][(p / CPR) * ROWB + (p % CPR) * 16]) = gq[i];
+        }
+    };
+    // one 32-query tile of the chunk in LDS buffer buf
+    auto tile = [&](int buf, int qt) {
+        bf16x8_t qa[RS];
 #pragma unroll
-        for (int st = 0; st < RS; ++st) qn[st] = load8(qnext + st * 16);
+        for (int st = 0; st < RS; ++st)
+            qa[st] = __builtin_bit_cast(bf16x8_t,
+                    *reinterpret_cast<const uint4*>(&lds[buf][(qt * 32 + col) * ROWB + (st * 2 + half) * 16]));
         // all key tiles' MFMAs first, each into its own accumulator, so the
         // max epilogue of one tile overlaps the matrix work of the next
         f32x16_t acc[NKT];
@@ -133,9 +167,22 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, Prefill
             for (int i = 2; i < 16; ++i) m = fmaxf(m, acc[t][i]);
             rm[t] = fmaxf(rm[t], m);
         }
+    };
+
+    load_chunk(c_begin);
+    store_chunk(0);
+    __syncthreads();
+    for (int c = c_begin; c < c_end; ++c) {
+        const int buf = (c - c_begin) & 1;
+        if (c + 1 < c_end) load_chunk(c + 1);   // in flight while this chunk is multiplied
+        if (active) {
 #pragma unroll
-        for (int st = 0; st < RS; ++st) qa[st] = qn[st];
+            for (int qt = 0; qt < kChunk / 32; ++qt) tile(buf, qt);
+        }
+        if (c + 1 < c_end) store_chunk(buf ^ 1);   // that buffer was last read before the previous barrier
+        __syncthreads();
     }
+    if (!active) return;
 
     uint32_t* out = keys + ((int64_t)l * a.S + s) * a.n;
 #pragma unroll
@@ -149,7 +196,7 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, Prefill
         const int64_t key = key0 + t * 32 + col;
         if (half == 0 && (col % BS) == 0 && key < gm.n_keys) {
             if ((live >> t) & 1u) atomicMax(out + key / BS, order_key(v));
-            else if (kv == 0) atomicOr(a.err, DEVERR_TABLE);
+            else if (kv == 0 && part == 0) atomicOr(a.err, DEVERR_TABLE);
         }
     }
 }
@@ -165,22 +212,29 @@ __global__ __launch_bounds__(256) void keys_to_scores_kernel(uint32_t* p, int64_
     if (i < n) reinterpret_cast<float*>(p)[i] = key_to_float(p[i]);
 }
 
-template <int RS, int NKT, int BS>
+template <int R, int NKT, int BS>
 void launch_t(const ScoreArgs& a, const PrefillGeom& gm, uint32_t* keys, hipStream_t st) {
-    const int64_t wgs = gm.groups * a.Hk * a.S * a.n_layers;
-    score_prefill_kernel<RS, NKT, BS><<<(unsigned)wgs, 256, 0, st>>>(a, gm, keys);
+    const int64_t wgs = gm.groups * gm.q_split * a.Hk * a.S * a.n_layers;
+    score_prefill_kernel<R, NKT, BS><<<(unsigned)wgs, 256, 0, st>>>(a, gm, keys);
 }
 
-template <int RS, int NKT>
+template <int R, int NKT>
 void launch_bs(const ScoreArgs& a, const PrefillGeom& gm, uint32_t* keys, hipStream_t st) {
     switch (a.B) {
-        case 8: launch_t<RS, NKT, 8>(a, gm, keys, st); break;
-        case 16: launch_t<RS, NKT, 16>(a, gm, keys, st); break;
-        default: launch_t<RS, NKT, 32>(a, gm, keys, st); break;
+        case 8: launch_t<R, NKT, 8>(a, gm, keys, st); break;
+        case 16: launch_t<R, NKT, 16>(a, gm, keys, st); break;
+        default: launch_t<R, NKT, 32>(a, gm, keys, st); break;
     }
 }
 
-constexpr int kNKT = 4;
+// 32-key tiles per wave: the keys' B operands take NKT * R / 4 registers
+constexpr int nkt_for(int r) { return r == 128 ? 2 : 4; }
+
+// waves the launch aims for when it splits the query axis (two per SIMD)
+#ifndef PRED_PREFILL_TARGET_WAVES
+#define PRED_PREFILL_TARGET_WAVES 2048
+#endif
+constexpr int64_t kTargetWaves = PRED_PREFILL_TARGET_WAVES;
 
 }  // namespace
 
@@ -192,19 +246,26 @@ hipError_t launch_score_prefill(const ScoreArgs& a, hipStream_t st) {
     PrefillGeom gm;
     const int g = a.Hq / a.Hk;
     gm.n_eff = a.M * g;
-    gm.q_tiles = (gm.n_eff + 31) / 32;
+    gm.chunks = (gm.n_eff + kChunk - 1) / kChunk;
     gm.n_keys = a.n * a.B;
-    const int64_t keys_per_group = (int64_t)kWaves * kNKT * 32;
+    const int64_t keys_per_group = (int64_t)kWaves * nkt_for(a.R) * 32;
     gm.groups = (gm.n_keys + keys_per_group - 1) / keys_per_group;
+    // split the query axis when the key groups alone give too few waves
+    const int64_t base_waves = gm.groups * a.Hk * a.S * a.n_layers * kWaves;
+    int64_t split = (kTargetWaves + base_waves - 1) / base_waves;
+    if (split > gm.chunks) split = gm.chunks;
+    if (split < 1) split = 1;
+    gm.chunks_per_part = (int)((gm.chunks + split - 1) / split);
+    gm.q_split = (gm.chunks + gm.chunks_per_part - 1) / gm.chunks_per_part;   // no empty parts
     uint32_t* keys = reinterpret_cast<uint32_t*>(a.scores);
     const int64_t total = (int64_t)a.n_layers * a.S * a.n;
     const unsigned fill_grid = (unsigned)((total + 255) / 256);
     fill_u32_kernel<<<fill_grid, 256, 0, st>>>(keys, total, 0u);
     switch (a.R) {
-        case 16: launch_bs<1, kNKT>(a, gm, keys, st); break;
-        case 32: launch_bs<2, kNKT>(a, gm, keys, st); break;
-        case 64: launch_bs<4, kNKT>(a, gm, keys, st); break;
-        default: launch_bs<8, kNKT>(a, gm, keys, st); break;
+        case 16: launch_bs<16, nkt_for(16)>(a, gm, keys, st); break;
+        case 32: launch_bs<32, nkt_for(32)>(a, gm, keys, st); break;
+        case 64: launch_bs<64, nkt_for(64)>(a, gm, keys, st); break;
+        default: launch_bs<128, nkt_for(128)>(a, gm, keys, st); break;
     }
     keys_to_scores_kernel<<<fill_grid, 256, 0, st>>>(keys, total);
     return hipGetLastError();
