@@ -14,10 +14,21 @@
 // the epilogue and written either densely (project_q) or into the A_g slot the
 // block table names, transposing [B, Hk] -> [Hk, B] (project_kv_block).
 //
+// Small calls (a decode step projects ~1000-4000 vectors, too few 16-vector
+// tiles to give every SIMD a wave) split the head_dim sum instead: the four
+// waves of a workgroup take a quarter of head_dim each for the same 16x16
+// tile, so each runs a quarter of the MFMA chain, and wave 0 adds the three
+// other float64 partials from LDS before the one rounding.
+//
 // Fallback (head_dim not in {32, 64, 128, 256} or r not a multiple of 16): one
 // lane per vector with float64 FMAs, P read through the scalar cache.
 #include "common.h"
 #include "kernels.h"
+
+// tile count below which a call splits head_dim across a workgroup's waves
+#ifndef PRED_PROJ_SPLITK_BELOW
+#define PRED_PROJ_SPLITK_BELOW 1024
+#endif
 
 namespace pred {
 
@@ -189,12 +200,94 @@ __global__ __launch_bounds__(256) void project_mfma_kernel(const uint16_t* __res
     }
 }
 
+// DW consecutive bf16 input values as DW / 2 packed words (DW in {2, 4, 8, 16}).
+template <int DW>
+__device__ inline void load_words(const uint16_t* p, uint32_t (&wd)[DW / 2]) {
+    if constexpr (DW >= 8) {
+#pragma unroll
+        for (int c = 0; c < DW / 8; ++c) {
+            const uint4 v = reinterpret_cast<const uint4*>(p)[c];
+            wd[4 * c] = v.x; wd[4 * c + 1] = v.y; wd[4 * c + 2] = v.z; wd[4 * c + 3] = v.w;
+        }
+    } else if constexpr (DW == 4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        wd[0] = v.x; wd[1] = v.y;
+    } else {
+        wd[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+}
+
+// One workgroup per (16-vector tile, 16-column tile); wave w sums head_dim
+// values [w*D/4, (w+1)*D/4), lane group q the DW of them starting at
+// w*D/4 + q*DW (DW = D/16 k-steps per wave).
+template <int DW>
+__global__ __launch_bounds__(256) void project_splitk_kernel(const uint16_t* __restrict__ in,
+                                                             const double* __restrict__ pf, OutMap om,
+                                                             int64_t n_vec, int64_t units) {
+    __shared__ f64x4_t part[3][64];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int64_t unit = blockIdx.x;
+    if (unit >= units) return;   // whole workgroup
+    const int D = 16 * DW;
+    const int R = om.R;
+    const int jtiles = R >> 4;
+    const int jt = (int)(unit % jtiles);
+    const int64_t v0 = (unit / jtiles) * 16;
+    const int col = lane & 15;
+    const int q = lane >> 4;
+    const int j = jt * 16 + col;
+    const int k0 = w * 4 * DW + q * DW;   // this lane's first head_dim index
+    const int64_t row_in = (v0 + col) < n_vec ? (v0 + col) : n_vec - 1;   // tail rows computed, not stored
+
+    uint32_t wd[DW / 2];
+    load_words<DW>(in + row_in * D + k0, wd);
+    double pb[DW];
+#pragma unroll
+    for (int s = 0; s < DW; ++s) pb[s] = pf[(int64_t)(k0 + s) * R + j];
+
+    f64x4_t acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int e = 0; e < DW / 2; ++e) {
+        acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_lo(wd[e]), pb[2 * e], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_hi(wd[e]), pb[2 * e + 1], acc1, 0, 0, 0);
+    }
+    f64x4_t acc = acc0 + acc1;
+    if (w > 0) part[w - 1][lane] = acc;
+    __syncthreads();
+    if (w > 0) return;
+    acc += part[0][lane];
+    acc += part[1][lane];
+    acc += part[2][lane];
+    // acc[v] of lane group q is output (row v0 + q + 4v, column j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int64_t row = v0 + q + 4 * v;
+        if (row < n_vec) {
+            const int64_t off = om.row_offset(row);
+            if (off >= 0) om.out[off + j] = f64_to_bf16_rne(acc[v]);
+            else if (col == 0 && jt == 0) atomicOr(om.err, DEVERR_TABLE);
+        }
+    }
+}
+
 bool mfma_path(int D, int R) { return (D == 32 || D == 64 || D == 128 || D == 256) && R % 16 == 0; }
 
 hipError_t launch_mfma(const uint16_t* in, const double* pf, const OutMap& om, int64_t n_vec, int D,
                        hipStream_t stream) {
     const int64_t vtiles = (n_vec + 15) / 16;
     const int jtiles = om.R / 16;
+    if (vtiles * jtiles < PRED_PROJ_SPLITK_BELOW) {
+        // too few tiles to occupy the SIMDs: split head_dim over a workgroup's waves
+        const int64_t units = vtiles * jtiles;
+        switch (D) {
+            case 32: project_splitk_kernel<2><<<(unsigned)units, 256, 0, stream>>>(in, pf, om, n_vec, units); break;
+            case 64: project_splitk_kernel<4><<<(unsigned)units, 256, 0, stream>>>(in, pf, om, n_vec, units); break;
+            case 128: project_splitk_kernel<8><<<(unsigned)units, 256, 0, stream>>>(in, pf, om, n_vec, units); break;
+            default: project_splitk_kernel<16><<<(unsigned)units, 256, 0, stream>>>(in, pf, om, n_vec, units); break;
+        }
+        return hipGetLastError();
+    }
     // about two waves per SIMD when there is that much work, one vector tile per wave otherwise
     int64_t vt = (vtiles * jtiles) / 2048;
     if (vt < 1) vt = 1;
