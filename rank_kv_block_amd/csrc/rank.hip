@@ -2,26 +2,17 @@
 // (predictor.rs page, module doc: scores only rank eviction victims; the
 // qsa_select.rs page's host top-k breaks ties toward the lower index).
 //
-// Scores map to order-preserving uint32 keys (-0 == +0, NaN first).  A segment
-// of up to 8192 keys is sorted inside one workgroup by an LSD radix sort over
-// eight 4-bit digits.  Items sit in blocked order (thread t owns positions
-// t*IPT .. t*IPT+IPT-1), so a pass is stable if each thread ranks its own items
-// in order and (digit, thread) counts are scanned digit-major:
-//   * a thread counts its items per digit in one packed register (sixteen
-//     4-bit counters in 64 bits, IPT <= 15) -- no cross-lane work;
-//   * the counts, as eight words of two 16-bit halves, are prefix-summed across
-//     the wave with DPP row shifts and row broadcasts, across the waves through
-//     one small LDS table, and across digits from the grand totals;
-//   * items are scattered as (key, index) pairs into one of two LDS buffers and
-//     read back in blocked order.
-// That is two barriers and about sixteen LDS instructions per thread and pass.
-// A pass whose digit is the same for every item (common for the high digits of
-// scores in a narrow range) is the identity and is skipped.  The first pass
-// starts in index order, so equal keys end in index order.
+// Scores map to order-preserving uint32 keys (-0 == +0, NaN first) and are
+// sorted as 64-bit (key << 32 | index) composites.  The composites are all
+// distinct and order exactly as the stable sort must, so any correct sort of
+// them -- stable or not -- gives the stable order.
 //
-// Segments over 2048 keys use every CU instead of one per segment:
-//   1. chunks of 1024 keys are sorted as above, one workgroup each, and written
-//      as sorted runs of keys and of their indexes;
+// A segment of up to 2048 keys is sorted inside one workgroup by a bitonic
+// network (rank_bitonic_kernel: registers, in-wave lane exchanges and, for the
+// largest strides only, LDS).  Longer segments use every CU instead of one per
+// segment:
+//   1. chunks of 1024 keys are sorted the same way, one workgroup each, and
+//      written as sorted runs of keys and of their indexes;
 //   2. runs are merged in groups of up to 8192 keys by counting: one workgroup
 //      per run loads its group's keys into LDS, and each element's place in the
 //      group is its index in its own run plus, for every other run, how many of
@@ -29,10 +20,9 @@
 //      indexes (an earlier chunk) also keys equal to it.  A branch-free binary
 //      search over the run (padded to 1024 with keys above every real one)
 //      counts them;
-//   3. groups (segments over 8192 keys) are merged pairwise as 64-bit
-//      (key << 32 | index) composites, which are distinct and order exactly as
-//      the stable sort must; each element finds its place in the merged run by
-//      binary search in the other run.
+//   3. groups (segments over 8192 keys) are merged pairwise as composites; each
+//      element finds its place in the merged run by binary search in the other
+//      run.
 #include "common.h"
 #include "kernels.h"
 
@@ -40,191 +30,129 @@ namespace pred {
 
 namespace {
 
-constexpr int kMaxLdsItems = 8192;   // keys one workgroup sorts or merges in LDS
-#ifndef PRED_RANK_CHUNK
-#define PRED_RANK_CHUNK 1024
-#endif
-constexpr int kChunk = PRED_RANK_CHUNK;   // keys per sorted run of step 1
+constexpr int kMaxLdsItems = 8192;   // keys of one step-2 group, merged in LDS
+constexpr int kChunk = 1024;         // keys per sorted run of step 1 (measured best of 512 / 1024 / 2048)
 constexpr int kSingle = 2048;        // up to this many keys a segment is sorted by one workgroup
+constexpr int kMergeTPB = 1024;      // step-2 threads per workgroup (one key of its run each)
 
-// step 1 workgroup shape for a chunk (waves x keys per thread = kChunk / 64) and
-// step 2 threads per workgroup
-#ifndef PRED_RANK_NW
-#define PRED_RANK_NW 4
-#define PRED_RANK_IPT 4
-#endif
-#ifndef PRED_RANK_MERGE_TPB
-#define PRED_RANK_MERGE_TPB 1024
-#endif
-static_assert(PRED_RANK_NW * 64 * PRED_RANK_IPT == kChunk, "a step-1 workgroup sorts one chunk");
-static_assert(PRED_RANK_MERGE_TPB <= kChunk, "a step-2 thread places at least one key of its run");
-
-template <int CTRL, int ROW_MASK>
-__device__ inline uint32_t dpp(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
+// Sorting network for one chunk of CH keys (power of two, 256..2048), 4 per
+// thread in blocked order (thread t holds positions 4t .. 4t+3).  Values are
+// (key << 32 | index) composites, all distinct, so the unstable network yields
+// exactly the stable order.  Bitonic stage (k, j) pairs positions p and p ^ j
+// inside runs of k; the lower position keeps the min when its run ascends
+// ((p & k) == 0).  j = 1, 2 pair registers of one thread; j = 4 .. 128 pair
+// lanes of one wave (lane distance j / 4: DPP for 1 and 2, swizzles for 4 to
+// 16, a permute for 32); j >= 256 pairs waves, through LDS (two buffers, so one
+// barrier per such stage).
+template <int M>
+__device__ inline uint32_t lane_xor_u32(uint32_t v) {
+    if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);
+    else if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true);
+    else if constexpr (M <= 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (M << 10) | 0x1F);   // xor within 32 lanes
+    else return (uint32_t)__shfl_xor((int)v, M);
 }
 
-// Inclusive prefix sum over the 64 lanes (packed 16-bit halves add independently).
-__device__ inline uint32_t wave_incl_scan(uint32_t v) {
-    v += dpp<0x111, 0xF>(v);   // row_shr:1
-    v += dpp<0x112, 0xF>(v);   // row_shr:2
-    v += dpp<0x114, 0xF>(v);   // row_shr:4
-    v += dpp<0x118, 0xF>(v);   // row_shr:8
-    v += dpp<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
-    v += dpp<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
-    return v;
+template <int M>
+__device__ inline uint64_t lane_xor_u64(uint64_t v) {
+    const uint32_t lo = lane_xor_u32<M>((uint32_t)v);
+    const uint32_t hi = lane_xor_u32<M>((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
 }
 
-// Inclusive prefix sum over lanes 0..15 (row 0); other rows get their own.
-__device__ inline uint32_t row_incl_scan(uint32_t v) {
-    v += dpp<0x111, 0xF>(v);
-    v += dpp<0x112, 0xF>(v);
-    v += dpp<0x114, 0xF>(v);
-    v += dpp<0x118, 0xF>(v);
-    return v;
-}
-
-// o[i] for a per-lane i in 0..7, as a tree of selects on registers.  The
-// words are made opaque first: otherwise the compiler turns the selects back
-// into an indexed array and places it in LDS (or scratch), costing a round trip
-// per item.
-__device__ inline uint32_t select8(const uint32_t (&o)[8], uint32_t i) {
-    uint32_t r[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        r[k] = o[k];
-        asm volatile("" : "+v"(r[k]));
-    }
-    const uint32_t a0 = (i & 1u) ? r[1] : r[0];
-    const uint32_t a1 = (i & 1u) ? r[3] : r[2];
-    const uint32_t a2 = (i & 1u) ? r[5] : r[4];
-    const uint32_t a3 = (i & 1u) ? r[7] : r[6];
-    const uint32_t b0 = (i & 2u) ? a1 : a0;
-    const uint32_t b1 = (i & 2u) ? a3 : a2;
-    return (i & 4u) ? b1 : b0;
-}
-
-// One workgroup per (segment, chunk) of up to CAP = 64*NW*IPT keys, NW <= 16.
-template <int NW, int IPT>
-__global__ __launch_bounds__(NW * 64) void rank_lds_kernel(const float* __restrict__ scores, int64_t n,
-                                                           int64_t chunk_len, int nchunks,
-                                                           int32_t* __restrict__ victims,
-                                                           uint32_t* __restrict__ run_keys,
-                                                           uint32_t* __restrict__ run_idx) {
-    static_assert(IPT <= 15 && IPT % 2 == 0, "packed 4-bit counters hold at most 15 items per thread");
-    static_assert(NW <= 16, "the cross-wave scan runs in one DPP row");
-    constexpr int T = NW * 64;
-    constexpr int CAP = T * IPT;
-    __shared__ __align__(16) uint2 kvb[2][CAP];       // (key, index) pairs, double-buffered
-    __shared__ __align__(16) uint4 wsum[2][NW][2];    // per-wave digit totals, double-buffered
-
-    const int t = threadIdx.x;
+template <int CH, int K, int J>
+__device__ inline void bitonic_stage(uint64_t (&x)[4], uint64_t (*xb)[CH], int& lb, int t) {
     const int lane = t & 63;
-    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int w = t >> 6;
+    if constexpr (J <= 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if ((e & J) == 0) {
+                const bool asc = ((4 * t + e) & K) == 0;
+                const uint64_t a = x[e], b = x[e | J];
+                const uint64_t lo = a < b ? a : b, hi = a < b ? b : a;
+                x[e] = asc ? lo : hi;
+                x[e | J] = asc ? hi : lo;
+            }
+        }
+    } else {
+        const bool asc = ((4 * t) & K) == 0;   // K >= 8: the same for the thread's four positions
+        uint64_t y[4];
+        bool lower;
+        if constexpr (J < 256) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = lane_xor_u64<J / 4>(x[e]);
+            lower = (lane & (J / 4)) == 0;
+        } else {
+            uint64_t* buf = xb[lb];
+            *reinterpret_cast<uint4*>(&buf[4 * t]) = make_uint4((uint32_t)x[0], (uint32_t)(x[0] >> 32),
+                                                                (uint32_t)x[1], (uint32_t)(x[1] >> 32));
+            *reinterpret_cast<uint4*>(&buf[4 * t + 2]) = make_uint4((uint32_t)x[2], (uint32_t)(x[2] >> 32),
+                                                                    (uint32_t)x[3], (uint32_t)(x[3] >> 32));
+            __syncthreads();
+            const int pt = t ^ (J / 4);   // partner thread, the same four offsets
+            const uint4 u0 = *reinterpret_cast<const uint4*>(&buf[4 * pt]);
+            const uint4 u1 = *reinterpret_cast<const uint4*>(&buf[4 * pt + 2]);
+            y[0] = ((uint64_t)u0.y << 32) | u0.x;
+            y[1] = ((uint64_t)u0.w << 32) | u0.z;
+            y[2] = ((uint64_t)u1.y << 32) | u1.x;
+            y[3] = ((uint64_t)u1.w << 32) | u1.z;
+            lb ^= 1;
+            lower = (w & (J / 256)) == 0;
+        }
+        const bool keep_min = lower == asc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint64_t a = x[e], b = y[e];
+            x[e] = (keep_min == (a < b)) ? a : b;
+        }
+    }
+}
+
+template <int CH, int K, int J>
+__device__ inline void bitonic_js(uint64_t (&x)[4], uint64_t (*xb)[CH], int& lb, int t) {
+    bitonic_stage<CH, K, J>(x, xb, lb, t);
+    if constexpr (J > 1) bitonic_js<CH, K, J / 2>(x, xb, lb, t);
+}
+
+template <int CH, int K>
+__device__ inline void bitonic_ks(uint64_t (&x)[4], uint64_t (*xb)[CH], int& lb, int t) {
+    bitonic_js<CH, K, K / 2>(x, xb, lb, t);
+    if constexpr (K < CH) bitonic_ks<CH, K * 2>(x, xb, lb, t);
+}
+
+// One workgroup per (segment, chunk) of up to CH keys.
+template <int CH>
+__global__ __launch_bounds__(CH / 4) void rank_bitonic_kernel(const float* __restrict__ scores, int64_t n,
+                                                              int64_t chunk_len, int nchunks,
+                                                              int32_t* __restrict__ victims,
+                                                              uint32_t* __restrict__ run_keys,
+                                                              uint32_t* __restrict__ run_idx) {
+    static_assert(CH >= 256 && CH <= 2048 && (CH & (CH - 1)) == 0, "one to eight waves of four keys per lane");
+    __shared__ __align__(16) uint64_t xb[2][CH];
+    const int t = threadIdx.x;
     const int64_t seg = blockIdx.x / nchunks;
     const int64_t off = (int64_t)(blockIdx.x % nchunks) * chunk_len;
     const int len = (int)((n - off) < chunk_len ? (n - off) : chunk_len);
     const float* src = scores + seg * n + off;
-
-    uint32_t key[IPT], idx[IPT];
+    uint64_t x[4];
 #pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-        const int pos = t * IPT + j;
-        if (pos < len) {
-            key[j] = order_key(src[pos]);
-            idx[j] = (uint32_t)(off + pos);
-        } else {
-            key[j] = 0xFFFFFFFFu;  // above every real key: padding sorts last
-            idx[j] = 0xFFFFFFFFu;
-        }
+    for (int e = 0; e < 4; ++e) {
+        const int pos = 4 * t + e;
+        // padding sorts after every real key (key 0xFFFFFFFF is above the key of +inf)
+        x[e] = pos < len ? (((uint64_t)order_key(src[pos]) << 32) | (uint32_t)(off + pos)) : ~0ull;
     }
-
-    int buf = 0;
-    for (int pass = 0; pass < 8; ++pass) {
-        const int shift = 4 * pass;
-        const int wb = pass & 1;
-        // rank each item among this thread's earlier items with the same digit
-        uint64_t packed = 0;
-        uint32_t dig[IPT], rnk[IPT];
+    int lb = 0;
+    bitonic_ks<CH, 2>(x, xb, lb, t);
 #pragma unroll
-        for (int j = 0; j < IPT; ++j) {
-            const uint32_t d = (key[j] >> shift) & 15u;
-            dig[j] = d;
-            rnk[j] = (uint32_t)(packed >> (4 * d)) & 15u;
-            packed += 1ull << (4 * d);
-        }
-        // counts as eight words: word i = count(2i) | count(2i+1) << 16
-        uint32_t cnt[8], inc[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t pair = (uint32_t)(packed >> (8 * i)) & 0xFFu;
-            cnt[i] = (pair & 15u) | ((pair >> 4) << 16);
-            inc[i] = wave_incl_scan(cnt[i]);
-        }
-        if (lane == 63) {
-            wsum[wb][w][0] = make_uint4(inc[0], inc[1], inc[2], inc[3]);
-            wsum[wb][w][1] = make_uint4(inc[4], inc[5], inc[6], inc[7]);
-        }
-        __syncthreads();
-        // lanes 0..NW-1 scan the wave totals; every wave reads its prefix and the grand totals
-        uint4 t0 = make_uint4(0u, 0u, 0u, 0u), t1 = t0;
-        if (lane < NW) {
-            t0 = wsum[wb][lane][0];
-            t1 = wsum[wb][lane][1];
-        }
-        const uint32_t tw[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-        uint32_t base[8];
-        uint32_t grand[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t sc = row_incl_scan(tw[i]);
-            grand[i] = (uint32_t)__builtin_amdgcn_readlane((int)sc, NW - 1);
-            base[i] = w > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)sc, w - 1) : 0u;
-        }
-        // digit bases: exclusive prefix of the grand totals over digits 0..15
-        uint32_t run = 0;
-        bool identity = false;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t lo = grand[i] & 0xFFFFu, hi = grand[i] >> 16;
-            identity |= (lo == (uint32_t)CAP) | (hi == (uint32_t)CAP);
-            const uint32_t dlo = run;
-            const uint32_t dhi = run + lo;
-            run = dhi + hi;
-            base[i] += dlo | (dhi << 16);
-        }
-        if (identity) continue;   // uniform: one digit holds every item
-        // first destination of (digit, this thread)
-        uint32_t first[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) first[i] = base[i] + inc[i] - cnt[i];
-        uint2* dstb = kvb[buf];
-#pragma unroll
-        for (int j = 0; j < IPT; ++j) {
-            const uint32_t word = select8(first, dig[j] >> 1);
-            const uint32_t o = (dig[j] & 1u) ? (word >> 16) : (word & 0xFFFFu);
-            dstb[o + rnk[j]] = make_uint2(key[j], idx[j]);
-        }
-        __syncthreads();
-        const uint4* mine = reinterpret_cast<const uint4*>(dstb + t * IPT);
-#pragma unroll
-        for (int c = 0; c < IPT / 2; ++c) {
-            const uint4 v = mine[c];
-            key[2 * c] = v.x; idx[2 * c] = v.y;
-            key[2 * c + 1] = v.z; idx[2 * c + 1] = v.w;
-        }
-        buf ^= 1;
-    }
-
-#pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-        const int pos = t * IPT + j;
+    for (int e = 0; e < 4; ++e) {
+        const int pos = 4 * t + e;
         if (pos < len) {
+            const int64_t o = seg * n + off + pos;
             if (run_keys) {
-                run_keys[seg * n + off + pos] = key[j];
-                run_idx[seg * n + off + pos] = idx[j];
+                run_keys[o] = (uint32_t)(x[e] >> 32);
+                run_idx[o] = (uint32_t)x[e];
             } else {
-                victims[seg * n + off + pos] = (int32_t)idx[j];
+                victims[o] = (int32_t)(uint32_t)x[e];
             }
         }
     }
@@ -346,13 +274,6 @@ __global__ __launch_bounds__(256) void rank_merge_kernel(const uint64_t* __restr
     else out[seg * n + dst] = x;
 }
 
-template <int NW, int IPT>
-void launch_lds(const float* scores, int64_t n, int64_t chunk_len, int nchunks, int64_t n_seg,
-                int32_t* victims, uint32_t* run_keys, uint32_t* run_idx, hipStream_t st) {
-    rank_lds_kernel<NW, IPT><<<(unsigned)(n_seg * nchunks), NW * 64, 0, st>>>(scores, n, chunk_len, nchunks,
-                                                                              victims, run_keys, run_idx);
-}
-
 }  // namespace
 
 size_t rank_workspace_bytes(int64_t n, int64_t n_seg) {
@@ -364,12 +285,16 @@ size_t rank_workspace_bytes(int64_t n, int64_t n_seg) {
 hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int32_t* victims, void* ws,
                        hipStream_t st) {
     if (n <= 0 || n_seg <= 0) return hipSuccess;
-    if (n <= 512) {
-        launch_lds<1, 8>(scores, n, n, 1, n_seg, victims, nullptr, nullptr, st);
+    if (n <= 256) {
+        rank_bitonic_kernel<256><<<(unsigned)n_seg, 64, 0, st>>>(scores, n, n, 1, victims, nullptr, nullptr);
+        return hipGetLastError();
+    }
+    if (n <= 1024) {
+        rank_bitonic_kernel<1024><<<(unsigned)n_seg, 256, 0, st>>>(scores, n, n, 1, victims, nullptr, nullptr);
         return hipGetLastError();
     }
     if (n <= kSingle) {
-        launch_lds<4, 8>(scores, n, n, 1, n_seg, victims, nullptr, nullptr, st);
+        rank_bitonic_kernel<2048><<<(unsigned)n_seg, 512, 0, st>>>(scores, n, n, 1, victims, nullptr, nullptr);
         return hipGetLastError();
     }
     // workspace: run keys and run indexes (4 + 4 bytes per key), then for long
@@ -379,11 +304,12 @@ hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int32_t* v
     uint64_t* r0 = static_cast<uint64_t*>(ws);
     uint64_t* r1 = r0 + n * n_seg;
     const int nruns = (int)((n + kChunk - 1) / kChunk);
-    launch_lds<PRED_RANK_NW, PRED_RANK_IPT>(scores, n, kChunk, nruns, n_seg, nullptr, rk, ri, st);
+    rank_bitonic_kernel<kChunk><<<(unsigned)(n_seg * nruns), kChunk / 4, 0, st>>>(scores, n, kChunk, nruns, nullptr,
+                                                                                rk, ri);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t group = n < kMaxLdsItems ? n : kMaxLdsItems;
-    rank_count_merge_kernel<PRED_RANK_MERGE_TPB><<<(unsigned)(n_seg * nruns), PRED_RANK_MERGE_TPB, 0, st>>>(
+    rank_count_merge_kernel<kMergeTPB><<<(unsigned)(n_seg * nruns), kMergeTPB, 0, st>>>(
         rk, ri, n, group, nruns, victims, n <= kMaxLdsItems ? nullptr : r1);
     e = hipGetLastError();
     if (e != hipSuccess || n <= kMaxLdsItems) return e;
