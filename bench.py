@@ -155,7 +155,28 @@ def main():
     rk.pred_device_error(wl.h)
 
     step_s = (t1 - t0) / args.steps
-    score_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    score_each = sorted(a.elapsed_time(b) for a, b in ev)
+    score_ms = sum(score_each) / args.steps
+
+    # the same layers scored one per call (a per-layer decode loop), each layer in turn
+    per_layer = None
+    if nl > 1:
+        l0 = wl.layer0_for_step(0)
+        evl = []
+        for rep in range(3):
+            for li in range(nl):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                rk.pred_score_blocks(wl.h, l0 + li, wl.q_proj[li:li + 1], wl.tables, wl.scores[li:li + 1])
+                e1.record(stream)
+                evl.append((e0, e1))
+        torch.cuda.synchronize()
+        rk.pred_device_error(wl.h)
+        lt = sorted(a.elapsed_time(b) for a, b in evl)
+        med = lt[len(lt) // 2]
+        layer_bytes = c.S * c.n * c.slot_bytes
+        per_layer = {"calls": len(lt), "median_us": round(med * 1e3, 2), "min_us": round(lt[0] * 1e3, 2),
+                     "max_us": round(lt[-1] * 1e3, 2), "a_g_gbs_at_median": round(layer_bytes / (med * 1e-3) / 1e9, 1)}
     blocks = c.blocks_per_step
     a_g_bytes = blocks * c.slot_bytes
     aux_bytes = blocks * 8 + nl * c.S * c.M * c.Hq * c.R * 2      # table entry + score per block, q_proj
@@ -193,9 +214,13 @@ def main():
         "blocks_per_s": round(blocks / step_s, 1),
         "pct_hbm_peak_step": round(100.0 * a_g_bytes / step_s / 1e9 / HBM_PEAK_GBS, 2),
         "score_kernel_ms": round(score_ms, 4),
+        "score_kernel_us": {"median": round(score_each[len(score_each) // 2] * 1e3, 2),
+                            "min": round(score_each[0] * 1e3, 2), "max": round(score_each[-1] * 1e3, 2)},
         "score_kernel_path": "many_row" if many_row else "decode_stream",
         "roofline": roofline,
     }
+    if per_layer is not None:
+        out["score_per_layer_call"] = per_layer
     if not args.no_cpu_baseline:
         print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
