@@ -181,8 +181,8 @@ int pred_check_fit(const pred_dims* d, uint64_t free_bytes) {
 const char* pred_limits(void) {
     return "head_dim and r multiples of 8; r <= 256; head_dim <= 65536; 16-byte aligned q, q_proj and k "
            "buffers. Streaming decode scorer: r in {16,32,64,128} and block_size*r/8 a power of two <= 1024; "
-           "other shapes use a plain per-block kernel. Rank: n_blocks <= 2^31-1 (above 8192 per segment a "
-           "workspace of 16*n_blocks*n_segments bytes is needed).";
+           "other shapes use a plain per-block kernel. Rank: n_blocks <= 2^31-1; above 2048 per segment a "
+           "workspace of 8*n_blocks*n_segments bytes is needed (16*n_blocks*n_segments above 8192).";
 }
 
 const char* pred_version(void) { return "rank_kv_block_amd 0.1 (gfx950)"; }
