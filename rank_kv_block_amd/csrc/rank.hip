@@ -20,8 +20,9 @@
 //      indexes (an earlier chunk) also keys equal to it.  A branch-free binary
 //      search over the run (padded to 1024 with keys above every real one)
 //      counts them;
-//   3. groups (segments over 8192 keys) are merged pairwise as composites; each
-//      element finds its place in the merged run by binary search in the other
+//   3. rows over 8192 keys repeat step 2 on the sorted groups: up to four runs
+//      of 8192 (128 KiB of keys in LDS); rows over 32768 then merge runs
+//      pairwise, each element finding its place by binary search in the other
 //      run.
 #include "common.h"
 #include "kernels.h"
@@ -34,6 +35,7 @@ constexpr int kMaxLdsItems = 8192;   // keys of one step-2 group, merged in LDS
 constexpr int kChunk = 1024;         // keys per sorted run of step 1 (measured best of 512 / 1024 / 2048)
 constexpr int kSingle = 2048;        // up to this many keys a segment is sorted by one workgroup
 constexpr int kMergeTPB = 1024;      // step-2 threads per workgroup (one key of its run each)
+constexpr int kMaxGroup2 = 32768;    // keys of one second-level group (128 KiB of LDS)
 
 // Sorting network for one chunk of CH keys (power of two, 256..2048), 4 per
 // thread in blocked order (thread t holds positions 4t .. 4t+3).  Values are
@@ -158,27 +160,33 @@ __global__ __launch_bounds__(CH / 4) void rank_bitonic_kernel(const float* __res
     }
 }
 
-// Step 2: one workgroup per (segment, run).  Runs of kChunk keys, grouped by
-// group_len (a multiple of kChunk, at most kMaxLdsItems); the output is the group
-// sorted, as victims when one group spans the segment, else as composites.
-template <int TPB>
-__global__ __launch_bounds__(TPB) void rank_count_merge_kernel(const uint32_t* __restrict__ run_keys,
-                                                               const uint32_t* __restrict__ run_idx, int64_t n,
-                                                               int64_t group_len, int nruns,
-                                                               int32_t* __restrict__ victims,
-                                                               uint64_t* __restrict__ out) {
-    constexpr int G = kMaxLdsItems / kChunk;   // runs per group, at most
-    constexpr int E = kChunk / TPB;            // elements of the run per thread
-    constexpr int L = kMaxLdsItems / TPB;      // group keys loaded per thread
-    __shared__ uint32_t gk[kMaxLdsItems];
+// Steps 2 and 3: merges by counting.  Sorted runs of RL keys (with their
+// indexes) are merged G at a time; a group's keys sit in LDS (G*RL*4 bytes: 32
+// KiB for 8 runs of 1024, 128 KiB for 4 runs of 8192).  One workgroup places TPB
+// consecutive elements of one run; the output is the group sorted, as victims
+// when one group spans the segment, else as keys and indexes again.
+template <int RL, int G, int TPB>
+__global__ __launch_bounds__(TPB) void rank_count_merge_kernel(const uint32_t* __restrict__ in_keys,
+                                                               const uint32_t* __restrict__ in_idx, int64_t n,
+                                                               int nruns, int32_t* __restrict__ victims,
+                                                               uint32_t* __restrict__ out_keys,
+                                                               uint32_t* __restrict__ out_idx) {
+    constexpr int GL = G * RL;       // keys of a full group
+    constexpr int PPR = RL / TPB;    // workgroups per run
+    constexpr int L = GL / TPB;      // group keys each thread loads
+    static_assert(RL % TPB == 0 && GL % TPB == 0, "whole workgroups per run and per group");
+    extern __shared__ uint32_t gk[];
     const int t = threadIdx.x;
-    const int64_t seg = blockIdx.x / nruns;
-    const int run = (int)(blockIdx.x % nruns);
-    const int64_t run0 = (int64_t)run * kChunk;                       // run start in the segment
-    const int64_t g0 = (run0 / group_len) * group_len;                // group start
-    const int glen = (int)((n - g0) < group_len ? (n - g0) : group_len);
-    const int own = (int)((run0 - g0) / kChunk);
-    const uint32_t* src = run_keys + seg * n + g0;
+    const int64_t per_seg = (int64_t)nruns * PPR;
+    const int64_t seg = blockIdx.x / per_seg;
+    const int64_t rem = blockIdx.x - seg * per_seg;
+    const int run = (int)(rem / PPR);
+    const int piece = (int)(rem - (int64_t)run * PPR);
+    const int64_t run0 = (int64_t)run * RL;                 // run start in the segment
+    const int64_t g0 = (run0 / GL) * GL;                    // group start
+    const int glen = (int)((n - g0) < GL ? (n - g0) : GL);
+    const int own = (int)((run0 - g0) / RL);
+    const uint32_t* src = in_keys + seg * n + g0;
     {
         // the group's keys, padded to G full runs with a key above every real one
         // (order keys never exceed that of +inf); clamped indexes keep every load
@@ -197,88 +205,96 @@ __global__ __launch_bounds__(TPB) void rank_count_merge_kernel(const uint32_t* _
     }
     __syncthreads();
 
-    const int rlen = (glen - own * kChunk) < kChunk ? (glen - own * kChunk) : kChunk;
-    uint32_t x[E];
-    int pos[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int i = t + TPB * e;
-        x[e] = gk[own * kChunk + (i < rlen ? i : 0)];
-        pos[e] = i;   // the elements of its own run before it
-    }
+    const int rlen = (glen - own * RL) < RL ? (glen - own * RL) : RL;
+    const int i = piece * TPB + t;                           // this thread's element of its run
+    const uint32_t x = gk[own * RL + (i < rlen ? i : 0)];
+    int pos = i;                                             // the elements of its own run before it
     // every run is searched (the own run too, its count discarded): no branch, so
-    // the G * E searches are independent chains of LDS reads that interleave
+    // the G searches are independent chains of LDS reads that interleave
 #pragma unroll
     for (int r = 0; r < G; ++r) {
-        const uint32_t bias = r < own ? 1u : 0u;   // earlier run: equal keys count as well
-        const uint32_t* a = gk + r * kChunk;
-        uint32_t xr[E];
-        int lo[E];
+        const uint32_t xr = x + (r < own ? 1u : 0u);         // earlier run: equal keys count as well
+        const uint32_t* a = gk + r * RL;                     // (no overflow: x <= order key of +inf)
+        int lo = 0;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            xr[e] = x[e] + bias;                   // no overflow: x <= order key of +inf
-            lo[e] = 0;
-        }
-#pragma unroll
-        for (int step = kChunk / 2; step >= 1; step >>= 1) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) lo[e] += a[lo[e] + step - 1] < xr[e] ? step : 0;
-        }
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            lo[e] += a[lo[e]] < xr[e] ? 1 : 0;     // lo <= kChunk - 1 before this
-            pos[e] += r == own ? 0 : lo[e];
-        }
+        for (int step = RL / 2; step >= 1; step >>= 1) lo += a[lo + step - 1] < xr ? step : 0;
+        lo += a[lo] < xr ? 1 : 0;                            // lo <= RL - 1 before this
+        pos += r == own ? 0 : lo;
     }
-    const bool whole = g0 == 0 && glen == n;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int i = t + TPB * e;
-        if (i < rlen && pos[e] < glen) {   // pos < glen always holds; never write outside the group
-            const int64_t dst = seg * n + g0 + pos[e];
-            const uint32_t id = run_idx[seg * n + run0 + i];
-            if (whole) victims[dst] = (int32_t)id;
-            else out[dst] = ((uint64_t)x[e] << 32) | id;
+    if (i < rlen && pos < glen) {   // pos < glen always holds; never write outside the group
+        const int64_t dst = seg * n + g0 + pos;
+        const uint32_t id = in_idx[seg * n + run0 + i];
+        if (g0 == 0 && glen == n) {
+            victims[dst] = (int32_t)id;
+        } else {
+            out_keys[dst] = x;
+            out_idx[dst] = id;
         }
     }
 }
 
-// Merge sorted runs [base, base+run) and [base+run, base+2run) of every segment.
-__global__ __launch_bounds__(256) void rank_merge_kernel(const uint64_t* __restrict__ in,
-                                                         uint64_t* __restrict__ out,
+// Rows over 32768 keys: merge sorted runs [base, base+run) and [base+run,
+// base+2run) of every segment.  An element counts the other run's keys before
+// it by binary search: keys below it, and for the first run (lower indexes)
+// also keys equal to it.
+__global__ __launch_bounds__(256) void rank_merge_kernel(const uint32_t* __restrict__ in_keys,
+                                                         const uint32_t* __restrict__ in_idx,
+                                                         uint32_t* __restrict__ out_keys,
+                                                         uint32_t* __restrict__ out_idx,
                                                          int32_t* __restrict__ victims, int64_t n,
                                                          int64_t n_seg, int64_t run) {
     const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (gi >= n * n_seg) return;
     const int64_t seg = gi / n;
     const int64_t pos = gi - seg * n;
-    const uint64_t* row = in + seg * n;
+    const uint32_t* row = in_keys + seg * n;
     const int64_t base = (pos / (2 * run)) * (2 * run);
     const int64_t a_end = (base + run) < n ? (base + run) : n;
     const int64_t b_end = (base + 2 * run) < n ? (base + 2 * run) : n;
-    const uint64_t x = row[pos];
+    const uint32_t x = row[pos];
     int64_t lo, hi, mine;
-    if (pos < a_end) {  // count elements of B below x
-        lo = a_end; hi = b_end; mine = pos - base;
-    } else {            // count elements of A below x
-        lo = base; hi = a_end; mine = pos - a_end;
+    uint32_t xr;
+    if (pos < a_end) {  // keys of the second run below x
+        lo = a_end; hi = b_end; mine = pos - base; xr = x;
+    } else {            // keys of the first run at most x
+        lo = base; hi = a_end; mine = pos - a_end; xr = x + 1u;
     }
     const int64_t first = lo;
     while (lo < hi) {
         const int64_t mid = lo + ((hi - lo) >> 1);
-        if (row[mid] < x) lo = mid + 1;
+        if (row[mid] < xr) lo = mid + 1;
         else hi = mid;
     }
-    const int64_t dst = base + mine + (lo - first);
-    if (victims) victims[seg * n + dst] = (int32_t)(uint32_t)x;
-    else out[seg * n + dst] = x;
+    const int64_t dst = seg * n + base + mine + (lo - first);
+    const uint32_t id = in_idx[seg * n + pos];
+    if (victims) {
+        victims[dst] = (int32_t)id;
+    } else {
+        out_keys[dst] = x;
+        out_idx[dst] = id;
+    }
+}
+
+template <int RL, int G, int TPB>
+hipError_t launch_count_merge(const uint32_t* ik, const uint32_t* ii, int64_t n, int64_t n_seg, int32_t* victims,
+                              uint32_t* ok, uint32_t* oi, hipStream_t st) {
+    const int nruns = (int)((n + RL - 1) / RL);
+    const size_t lds = (size_t)G * RL * sizeof(uint32_t);
+    if (lds > 65536) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rank_count_merge_kernel<RL, G, TPB>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    rank_count_merge_kernel<RL, G, TPB><<<(unsigned)(n_seg * nruns * (RL / TPB)), TPB, lds, st>>>(
+        ik, ii, n, nruns, victims, ok, oi);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 size_t rank_workspace_bytes(int64_t n, int64_t n_seg) {
     if (n <= kSingle || n_seg <= 0) return 0;
-    // sorted runs; segments over kMaxLdsItems keys also need a second buffer for the pairwise merges
+    // sorted runs as keys + indexes; longer rows ping-pong between two such buffers
     return (size_t)((n <= kMaxLdsItems ? 1 : 2) * n * n_seg) * sizeof(uint64_t);
 }
 
@@ -297,32 +313,34 @@ hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int32_t* v
         rank_bitonic_kernel<2048><<<(unsigned)n_seg, 512, 0, st>>>(scores, n, n, 1, victims, nullptr, nullptr);
         return hipGetLastError();
     }
-    // workspace: run keys and run indexes (4 + 4 bytes per key), then for long
-    // segments one more 8 bytes per key for the pairwise merges
-    uint32_t* rk = static_cast<uint32_t*>(ws);
-    uint32_t* ri = rk + n * n_seg;
-    uint64_t* r0 = static_cast<uint64_t*>(ws);
-    uint64_t* r1 = r0 + n * n_seg;
+    // workspace: buffer A = run keys then run indexes (4 + 4 bytes per key), and
+    // for rows over 8192 keys buffer B of the same shape
+    const int64_t total = n * n_seg;
+    uint32_t* ak = static_cast<uint32_t*>(ws);
+    uint32_t* ai = ak + total;
+    uint32_t* bk = ai + total;
+    uint32_t* bi = bk + total;
     const int nruns = (int)((n + kChunk - 1) / kChunk);
     rank_bitonic_kernel<kChunk><<<(unsigned)(n_seg * nruns), kChunk / 4, 0, st>>>(scores, n, kChunk, nruns, nullptr,
-                                                                                rk, ri);
+                                                                                ak, ai);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t group = n < kMaxLdsItems ? n : kMaxLdsItems;
-    rank_count_merge_kernel<kMergeTPB><<<(unsigned)(n_seg * nruns), kMergeTPB, 0, st>>>(
-        rk, ri, n, group, nruns, victims, n <= kMaxLdsItems ? nullptr : r1);
-    e = hipGetLastError();
+    // runs of 1024 -> groups of 8192 (the whole row when it is no longer)
+    e = launch_count_merge<kChunk, kMaxLdsItems / kChunk, kMergeTPB>(ak, ai, n, n_seg, victims, bk, bi, st);
     if (e != hipSuccess || n <= kMaxLdsItems) return e;
-    // sorted groups of kMaxLdsItems are in r1; merge them pairwise
-    uint64_t* in = r1;
-    uint64_t* outb = r0;
-    const unsigned grid = (unsigned)((n * n_seg + 255) / 256);
-    for (int64_t run = kMaxLdsItems; run < n; run *= 2) {
+    // runs of 8192 -> groups of 32768 (128 KiB of keys in LDS)
+    e = launch_count_merge<kMaxLdsItems, kMaxGroup2 / kMaxLdsItems, kMergeTPB>(bk, bi, n, n_seg, victims, ak, ai, st);
+    if (e != hipSuccess || n <= kMaxGroup2) return e;
+    // longer rows: pairwise merges of runs of 32768, 65536, ...
+    uint32_t *ik = ak, *ii = ai, *ok = bk, *oi = bi;
+    const unsigned grid = (unsigned)((total + 255) / 256);
+    for (int64_t run = kMaxGroup2; run < n; run *= 2) {
         const bool last = 2 * run >= n;
-        rank_merge_kernel<<<grid, 256, 0, st>>>(in, outb, last ? victims : nullptr, n, n_seg, run);
+        rank_merge_kernel<<<grid, 256, 0, st>>>(ik, ii, ok, oi, last ? victims : nullptr, n, n_seg, run);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        uint64_t* tmp = in; in = outb; outb = tmp;
+        uint32_t* tk = ik; ik = ok; ok = tk;
+        uint32_t* ti = ii; ii = oi; oi = ti;
     }
     return hipSuccess;
 }

@@ -180,7 +180,7 @@ def test_random_shape_parity(shape):
 @pytest.mark.parametrize("n,segs", [(1, 1), (5, 3), (64, 1), (256, 2), (257, 2), (513, 2), (1024, 3), (1025, 2), (2048, 4), (2049, 3),
                                     (3000, 5), (4095, 2),
                                     (8191, 1), (8192, 2), (8193, 1),
-                                    (16384, 1), (16385, 1), (24576, 3), (40000, 2), (65536, 1)])
+                                    (16384, 1), (16385, 1), (24576, 3), (32768, 2), (32769, 1), (40000, 2), (65536, 1), (100000, 1)])
 def test_rank_exact(n, segs):
     _say("rank", n, segs)
     rng = np.random.default_rng(n * 7 + segs)
