@@ -64,6 +64,24 @@ def test_projection_on_device_matches_oracle(D, R, seed):
         assert np.array_equal(rk.pred_copy_projection(p.handle), prng.projection(D, R, seed))
 
 
+@pytest.mark.parametrize("D,R,n_vec", [(32, 32, 20000), (64, 16, 17000), (128, 64, 16400), (256, 32, 9000),
+                                       (128, 32, 37), (256, 48, 300), (96, 24, 5000)])
+def test_project_q_sizes(D, R, n_vec):
+    """project_q alone, at sizes that take the streaming MFMA kernel (>= 1024 16x16 tiles), the
+    head_dim-split kernel (small calls) and the plain kernel (r not a multiple of 16 / other head_dim)."""
+    _say("project_q", D, R, n_vec)
+    rng = np.random.default_rng(D * 1000 + R + n_vec)
+    d = rk.dims(1, 1, 1, D, R, 16, 4)
+    seed = 4242 + D + R
+    with rk.Predictor(d, seed) as p:
+        P = prng.projection(D, R, seed)
+        q = _randn_bits(rng, (n_vec, 1, D))
+        qp = torch.empty((n_vec, 1, R), dtype=torch.bfloat16, device="cuda")
+        rk.pred_project_q(p.handle, _to_dev(q), qp)
+        torch.cuda.synchronize()
+        assert_ulp(_bits_np(qp), predictor.project_q(q, P), "q_proj")
+
+
 # ---------------------------------------------------------------- hand examples
 
 def _pad(a, shape):
@@ -122,6 +140,8 @@ SHAPES = [
     (1, 8, 2, 32, 16, 12, 60, 29, 2, 1, "identity"),       # block_size 12: plain per-block kernel
     (1, 16, 2, 64, 128, 32, 40, 37, 1, 1, "perm"),         # 1 KiB-wide kv regions: 16 load slots per wave
     (2, 32, 8, 128, 32, 16, 9000, 8200, 1, 1, "perm"),     # larger ragged case, two layers
+    (1, 8, 2, 256, 32, 16, 40, 21, 1, 1, "identity"),      # head_dim 256: widest MFMA projection tiles
+    (1, 8, 2, 96, 16, 16, 40, 20, 2, 1, "perm"),           # head_dim 96: plain projection kernel
     # many query rows: the MFMA scorer
     (1, 32, 8, 128, 64, 16, 300, 260, 1, 64, "perm"),      # prefill-chunk dims, ragged key tiles
     (2, 16, 4, 64, 32, 32, 150, 70, 2, 40, "perm"),        # block_size 32, two layers, two sequences
