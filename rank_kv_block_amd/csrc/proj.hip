@@ -245,6 +245,16 @@ __global__ __launch_bounds__(256) void project_splitk_kernel(const uint16_t* __r
     double pb[DW];
 #pragma unroll
     for (int s = 0; s < DW; ++s) pb[s] = pf[(int64_t)(k0 + s) * R + j];
+    // output offsets of this lane's four rows, looked up (block table) before the
+    // MFMA chain so the lookup's latency overlaps it
+    int64_t off[4];
+    if (w == 0) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t row = v0 + q + 4 * v;
+            off[v] = row < n_vec ? om.row_offset(row) : -2;
+        }
+    }
 
     f64x4_t acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -259,15 +269,12 @@ __global__ __launch_bounds__(256) void project_splitk_kernel(const uint16_t* __r
     acc += part[0][lane];
     acc += part[1][lane];
     acc += part[2][lane];
-    // acc[v] of lane group q is output (row v0 + q + 4v, column j)
+    // acc[v] of lane group q is output (row v0 + q + 4v, column j); off -1: invalid
+    // table entry, -2: tail row past n_vec
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-        const int64_t row = v0 + q + 4 * v;
-        if (row < n_vec) {
-            const int64_t off = om.row_offset(row);
-            if (off >= 0) om.out[off + j] = f64_to_bf16_rne(acc[v]);
-            else if (col == 0 && jt == 0) atomicOr(om.err, DEVERR_TABLE);
-        }
+        if (off[v] >= 0) om.out[off[v] + j] = f64_to_bf16_rne(acc[v]);
+        else if (off[v] == -1 && col == 0 && jt == 0) atomicOr(om.err, DEVERR_TABLE);
     }
 }
 
