@@ -156,7 +156,9 @@ int pred_score_blocks(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf
  *              +0, NaN before everything
  *   workspace  device scratch of at least pred_rank_workspace_bytes() bytes
  *              (may be NULL when that is 0)
- * n_blocks must be <= 2^31 - 1. */
+ * n_blocks and n_segments must be <= 2^31 - 1.  A call too large for one
+ * launch (over 2^31 - 1 workgroups) fails with PRED_ERR_OUT_OF_RANGE before
+ * anything is enqueued; the same holds for the other entry points. */
 int pred_rank_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments,
                       int32_t* victims, void* workspace, size_t ws_bytes, void* stream);
 

@@ -6,6 +6,10 @@
 
 namespace pred {
 
+// A launch takes at most 2^31 - 1 workgroups; a call that would need more is
+// rejected with hipErrorInvalidConfiguration before anything is enqueued.
+inline bool grid_fits(int64_t workgroups) { return workgroups >= 0 && workgroups <= 0x7FFFFFFF; }
+
 // ---- projections (proj.hip) ----------------------------------------------
 // out[v, :] = bf16(in[v, :] @ P) for n_vec rows of D bf16 (dense output [n_vec, R]).
 hipError_t launch_project_dense(const uint16_t* in, const double* pf, uint16_t* out, int64_t n_vec,

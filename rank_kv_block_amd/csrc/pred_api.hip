@@ -48,6 +48,8 @@ int ok() {
 }
 
 int hip_fail(hipError_t e, const char* what) {
+    if (e == hipErrorInvalidConfiguration)   // raised by the launchers themselves, before enqueueing
+        return fail(PRED_ERR_OUT_OF_RANGE, "%s: the call needs more than 2^31-1 workgroups; split it", what);
     return fail(PRED_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
@@ -292,7 +294,8 @@ int pred_rank_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t 
     if (n_blocks < 0 || n_segments < 0)
         return fail(PRED_ERR_OUT_OF_RANGE, "negative count (n_blocks %lld, n_segments %lld)", (long long)n_blocks,
                     (long long)n_segments);
-    if (n_blocks > 2147483647LL) return fail(PRED_ERR_OUT_OF_RANGE, "n_blocks above 2^31-1");
+    if (n_blocks > 2147483647LL || n_segments > 2147483647LL)
+        return fail(PRED_ERR_OUT_OF_RANGE, "n_blocks and n_segments must be <= 2^31-1");
     if (n_blocks == 0 || n_segments == 0) return ok();
     if (!scores || !victims) return fail(PRED_ERR_NULL_ARG, "scores or victims is NULL");
     const size_t need = pred::rank_workspace_bytes(n_blocks, n_segments);

@@ -284,6 +284,7 @@ hipError_t launch_mfma(const uint16_t* in, const double* pf, const OutMap& om, i
                        hipStream_t stream) {
     const int64_t vtiles = (n_vec + 15) / 16;
     const int jtiles = om.R / 16;
+    if (!grid_fits(vtiles * jtiles)) return hipErrorInvalidConfiguration;
     if (vtiles * jtiles < PRED_PROJ_SPLITK_BELOW) {
         // too few tiles to occupy the SIMDs: split head_dim over a workgroup's waves
         const int64_t units = vtiles * jtiles;
@@ -331,6 +332,7 @@ hipError_t launch_project_dense(const uint16_t* in, const double* pf, uint16_t* 
         return launch_mfma(in, pf, om, n_vec, D, stream);
     }
     const int rc = pick_rc(R, n_vec);
+    if (!grid_fits((n_vec + 255) / 256)) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)((n_vec + 255) / 256), (unsigned)(R / rc));
     switch (rc) {
         case 64: project_dense_kernel<64><<<grid, 256, 0, stream>>>(in, pf, out, n_vec, D, R); break;
@@ -351,6 +353,7 @@ hipError_t launch_project_paged(const uint16_t* k, const double* pf, uint16_t* a
         return launch_mfma(k, pf, om, n_vec, D, stream);
     }
     const int rc = pick_rc(R, n_vec);
+    if (!grid_fits((n_vec + 255) / 256)) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)((n_vec + 255) / 256), (unsigned)(R / rc));
 #define PRED_PAGED(RCV)                                                                                      \
     project_paged_kernel<RCV><<<grid, 256, 0, stream>>>(k, pf, a_first, table, n_vec, n_blocks, N, Hk, B, D, R, err)

@@ -301,6 +301,12 @@ size_t rank_workspace_bytes(int64_t n, int64_t n_seg) {
 hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int32_t* victims, void* ws,
                        hipStream_t st) {
     if (n <= 0 || n_seg <= 0) return hipSuccess;
+    // largest grids of the path this row length takes: the step-1 sort, the
+    // second merge level (8 workgroups per run of 8192) and the pairwise merges
+    const int64_t chunks = n <= kSingle ? 1 : (n + kChunk - 1) / kChunk;
+    if (!grid_fits(n_seg * chunks) || !grid_fits(n_seg * ((n + kMaxLdsItems - 1) / kMaxLdsItems) * 8) ||
+        !grid_fits((n * n_seg + 255) / 256))
+        return hipErrorInvalidConfiguration;
     if (n <= 256) {
         rank_bitonic_kernel<256><<<(unsigned)n_seg, 64, 0, st>>>(scores, n, n, 1, victims, nullptr, nullptr);
         return hipGetLastError();

@@ -439,11 +439,13 @@ hipError_t launch_score_decode_or_generic(const ScoreArgs& a, hipStream_t stream
     DecodeGeom gm;
     int ns, lpr, qh;
     if (decode_geometry(a, gm, ns, lpr, qh)) {
+        if (!grid_fits(gm.wgs_per_seq * a.S * a.n_layers)) return hipErrorInvalidConfiguration;
         if (ns == 16) launch_decode_ns<16>(a, gm, lpr, qh, stream);
         else if (ns == 4) launch_decode_ns<4>(a, gm, lpr, qh, stream);
         else launch_decode_ns<8>(a, gm, lpr, qh, stream);
     } else {
         const int64_t total = (int64_t)a.n_layers * a.S * a.n;
+        if (!grid_fits((total + 255) / 256)) return hipErrorInvalidConfiguration;
         score_generic_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(a);
     }
     return hipGetLastError();

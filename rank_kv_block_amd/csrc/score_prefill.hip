@@ -259,6 +259,8 @@ hipError_t launch_score_prefill(const ScoreArgs& a, hipStream_t st) {
     gm.q_split = (gm.chunks + gm.chunks_per_part - 1) / gm.chunks_per_part;   // no empty parts
     uint32_t* keys = reinterpret_cast<uint32_t*>(a.scores);
     const int64_t total = (int64_t)a.n_layers * a.S * a.n;
+    if (!grid_fits(gm.groups * gm.q_split * a.Hk * a.S * a.n_layers) || !grid_fits((total + 255) / 256))
+        return hipErrorInvalidConfiguration;
     const unsigned fill_grid = (unsigned)((total + 255) / 256);
     fill_u32_kernel<<<fill_grid, 256, 0, st>>>(keys, total, 0u);
     switch (a.R) {
