@@ -29,7 +29,7 @@ def _gpu():
     yield
 
 
-def _check_workload(name, l0=0, sample_blocks=128, full_layers=1, keep_per_layer=8, steps=2):
+def _check_workload(name, l0=0, sample_blocks=128, full_layers=1, keep_per_layer=8, steps=2, side_stream=False):
     from rank_kv_block_amd.workloads import CONFIGS, Workload
     import rank_kv_block_amd as rk
     c = CONFIGS[name]
@@ -45,9 +45,18 @@ def _check_workload(name, l0=0, sample_blocks=128, full_layers=1, keep_per_layer
     _say(name, "setup")
     wl = Workload(c, keep=keep)
     try:
-        _say(name, "steps", steps)
-        for _ in range(steps):
-            wl.step(l0)
+        _say(name, "steps", steps, "side stream" if side_stream else "")
+        if side_stream:
+            # every call enqueues on the stream it is given: run the step on a second
+            # stream, ordered after the set-up work of the current one
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+            for _ in range(steps):
+                wl.step(l0, stream=st)
+            st.synchronize()
+        else:
+            for _ in range(steps):
+                wl.step(l0)
         torch.cuda.synchronize()
         rk.pred_device_error(wl.h)
         P = rk.pred_copy_projection(wl.h)
@@ -116,3 +125,7 @@ def test_config_prefill_chunk():
 
 def test_config_long_context_70b():
     _check_workload("long_context_70b", l0=5, full_layers=1, keep_per_layer=16)
+
+
+def test_config_llama3_8b_decode_on_a_second_stream():
+    _check_workload("llama3_8b_decode", full_layers=1, sample_blocks=32, keep_per_layer=2, side_stream=True)
