@@ -147,6 +147,8 @@ SHAPES = [
     (2, 16, 4, 64, 32, 32, 150, 70, 2, 40, "perm"),        # block_size 32, two layers, two sequences
     (1, 8, 1, 64, 16, 8, 50, 45, 1, 33, "identity"),       # block_size 8, r = 16, one kv head
     (1, 16, 2, 128, 128, 16, 40, 33, 1, 9, "perm"),        # r = 128, 72 queries per kv head
+    (1, 8, 2, 64, 24, 16, 30, 20, 1, 6, "perm"),           # 24 queries per kv head at r = 24: plain kernel
+    (1, 8, 2, 64, 32, 12, 48, 20, 2, 5, "identity"),       # 20 queries per kv head, block_size 12: plain kernel
 ]
 
 
