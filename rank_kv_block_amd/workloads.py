@@ -14,8 +14,9 @@ The new blocks carry the same keys as at set-up, so a step rewrites identical
 low-rank keys and every step's outputs are the same: the outputs after a timed
 run can be checked against the oracle.
 
-Shapes and data follow the workload list of the block predictor's benchmark
-(Llama-3-8B-like and 70B-like head counts and dims; no model weights).
+Shapes are those of the decode, batched-decode, prefill and long-context cases
+the predictor serves (Llama-3-8B-like and 70B-like head counts and dims); all
+data is seeded and synthetic, with no model weights.
 """
 
 import hashlib
