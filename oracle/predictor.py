@@ -11,7 +11,7 @@ Notation: L layers, Hq query heads, Hk kv heads, g = Hq / Hk, D head_dim, R rank
 B block_size, N max_blocks; S sequences, n blocks per sequence, M query rows.
 All arrays are row-major.  bf16 tensors are uint16 bit patterns.
 
-Readings where the pages leave a step open (each is listed in the design doc too):
+Readings where the pages leave a step open:
 
 * accumulation: products and sums in float64, one RNE rounding to bf16;
 * GQA: query head h reads kv head floor(h / g);
