@@ -158,6 +158,30 @@ def main():
     score_each = sorted(a.elapsed_time(b) for a, b in ev)
     score_ms = sum(score_each) / args.steps
 
+    # per-call breakdown of a step, in a separate loop so the timed steps above
+    # carry no extra events: median of 20 steps per entry point
+    names = ["project_kv_block", "project_q", "score_blocks", "rank_victims"]
+    evs = {k: [] for k in names}
+    for i in range(20):
+        l0 = wl.layer0_for_step(i)
+        calls = [
+            lambda: rk.pred_project_kv_block(wl.h, l0, wl.k_new[l0:l0 + nl], wl.table_new[l0:l0 + nl]),
+            lambda: rk.pred_project_q(wl.h, wl.q[l0:l0 + nl], wl.q_proj),
+            lambda: rk.pred_score_blocks(wl.h, l0, wl.q_proj, wl.tables, wl.scores),
+            lambda: rk.pred_rank_victims(wl.h, wl.scores.view(nl * c.S, c.n), wl.victims, wl.workspace),
+        ]
+        for name, call in zip(names, calls):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            evs[name].append((e0, e1))
+    torch.cuda.synchronize()
+    breakdown = {}
+    for name in names:
+        t = sorted(a.elapsed_time(b) for a, b in evs[name])
+        breakdown[name] = round(t[len(t) // 2] * 1e3, 2)
+
     # the same layers scored one per call (a per-layer decode loop), each layer in turn
     per_layer = None
     if nl > 1:
@@ -219,6 +243,7 @@ def main():
         "score_kernel_path": "many_row" if many_row else "decode_stream",
         "roofline": roofline,
     }
+    out["step_breakdown_median_us"] = breakdown
     if per_layer is not None:
         out["score_per_layer_call"] = per_layer
     if not args.no_cpu_baseline:
