@@ -106,6 +106,8 @@ def main():
     ap.add_argument("--config", default="llama3_8b_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--per-layer-calls", action="store_true",
+                    help="also time the step's layers scored one layer per call (multi-layer workloads)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -184,7 +186,7 @@ def main():
 
     # the same layers scored one per call (a per-layer decode loop), each layer in turn
     per_layer = None
-    if nl > 1:
+    if nl > 1 and args.per_layer_calls:
         l0 = wl.layer0_for_step(0)
         evl = []
         for rep in range(3):
