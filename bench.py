@@ -183,6 +183,19 @@ def main():
     for name in names:
         t = sorted(a.elapsed_time(b) for a, b in evs[name])
         breakdown[name] = round(t[len(t) // 2] * 1e3, 2)
+    # the k lowest only (the eviction batch), k = 64: the same scores, the same workspace
+    k_sel = min(64, c.n)
+    sel_out = torch.empty((nl * c.S, k_sel), dtype=torch.int32, device="cuda")
+    evk = []
+    for i in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rk.pred_select_victims(wl.h, wl.scores.view(nl * c.S, c.n), k_sel, sel_out, wl.workspace)
+        e1.record(stream)
+        evk.append((e0, e1))
+    torch.cuda.synchronize()
+    tk = sorted(a.elapsed_time(b) for a, b in evk)
+    breakdown[f"select_victims_k{k_sel}"] = round(tk[len(tk) // 2] * 1e3, 2)
 
     # the same layers scored one per call (a per-layer decode loop), each layer in turn
     per_layer = None

@@ -162,6 +162,21 @@ int pred_score_blocks(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf
 int pred_rank_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments,
                       int32_t* victims, void* workspace, size_t ws_bytes, void* stream);
 
+/* The k lowest-scored blocks of every segment, in eviction order: row s of
+ * victims is exactly the first k entries of pred_rank_victims's row s (scores
+ * ascending, equal scores in ascending index order, -0 equal to +0, NaN
+ * first).  This is the step after the ranking (predictor.rs page, module doc:
+ * scores rank eviction victims; a cache evicts k blocks at a time).
+ *   scores     device, [n_segments, n_blocks] float32
+ *   k          0 <= k <= n_blocks (k = n_blocks is the full ranking)
+ *   victims    device, [n_segments, k] int32 output (row stride k)
+ *   workspace  as for pred_rank_victims (pred_rank_workspace_bytes(n_blocks,
+ *              n_segments) bytes; NULL when that is 0)
+ * Only each sorted run's first k places are merged, so small k costs less
+ * than the full ranking. */
+int pred_select_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments, int64_t k,
+                        int32_t* victims, void* workspace, size_t ws_bytes, void* stream);
+
 /* Workspace pred_rank_victims needs for this shape: 0 for n_blocks <= 2048
  * (each segment is sorted inside one workgroup), else 8 bytes per key for the
  * sorted runs, twice that for n_blocks > 8192 (pairwise merge buffers). */

@@ -25,6 +25,7 @@ Parity status per function (what pins it is listed in each module docstring):
                                                     q^T P P^T k, P = I logits, invariants)
 * ``predictor.rank_victims``                        pinned (sorted() on tiny inputs,
                                                     permutation validity, planted blocks)
+* ``predictor.select_victims``                      pinned (sorted() truncated to k)
 """
 
 from . import bf16, prng, predictor  # noqa: F401

@@ -146,3 +146,10 @@ def rank_victims(scores_f32):
     s = np.atleast_2d(np.asarray(scores_f32, dtype=np.float32))
     keys = order_key(s)
     return np.argsort(keys, axis=1, kind="stable").astype(np.int32)
+
+
+def select_victims(scores, k):
+    """The k lowest-scored blocks of every row in eviction order: by definition the
+    first k entries of ``rank_victims`` (the predictor page's module doc: scores only
+    rank eviction victims; a cache evicts a few blocks at a time)."""
+    return rank_victims(scores)[:, :k]

@@ -179,6 +179,19 @@ def pred_rank_victims(h, scores, victims, workspace=None, stream=None):
                                    ws_bytes, _stream(stream)))
 
 
+def pred_select_victims(h, scores, k, victims, workspace=None, stream=None):
+    """scores [n_segments, n_blocks] float32 -> victims [n_segments, k] int32: the k lowest of each row,
+    in eviction order (the first k of pred_rank_victims)."""
+    import torch
+    if scores.dim() != 2 or victims.dim() != 2 or victims.shape[0] != scores.shape[0] or victims.shape[1] != k:
+        raise ValueError("scores must be [n_segments, n_blocks] and victims [n_segments, k]")
+    n_seg, n = scores.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pred_select_victims(h, _ptr(scores, "scores", (torch.float32,)), n, n_seg, k,
+                                     _ptr(victims, "victims", (torch.int32,)), _ptr(workspace, "workspace"),
+                                     ws_bytes, _stream(stream)))
+
+
 # ------------------------------------------------------------------ inspection
 
 def pred_copy_projection(h):

@@ -37,7 +37,7 @@ const char* score_decode_path_name(const ScoreArgs& a);
 
 // ---- ranking (rank.hip) --------------------------------------------------
 size_t rank_workspace_bytes(int64_t n, int64_t n_seg);
-hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int32_t* victims, void* ws,
+hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int64_t k, int32_t* victims, void* ws,
                        hipStream_t stream);
 
 }  // namespace pred

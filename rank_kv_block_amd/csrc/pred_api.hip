@@ -288,24 +288,42 @@ int pred_score_blocks(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf
     return ok();
 }
 
-int pred_rank_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments, int32_t* victims,
-                      void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+
+// The k lowest of every segment, in eviction order; k = n_blocks is the full ranking.
+int rank_or_select(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments, int64_t k, int32_t* victims,
+                   void* workspace, size_t ws_bytes, void* stream, const char* what) {
     if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
     if (n_blocks < 0 || n_segments < 0)
         return fail(PRED_ERR_OUT_OF_RANGE, "negative count (n_blocks %lld, n_segments %lld)", (long long)n_blocks,
                     (long long)n_segments);
     if (n_blocks > 2147483647LL || n_segments > 2147483647LL)
         return fail(PRED_ERR_OUT_OF_RANGE, "n_blocks and n_segments must be <= 2^31-1");
-    if (n_blocks == 0 || n_segments == 0) return ok();
+    if (k < 0 || k > n_blocks)
+        return fail(PRED_ERR_OUT_OF_RANGE, "k (%lld) outside [0, n_blocks = %lld]", (long long)k, (long long)n_blocks);
+    if (n_blocks == 0 || n_segments == 0 || k == 0) return ok();
     if (!scores || !victims) return fail(PRED_ERR_NULL_ARG, "scores or victims is NULL");
     const size_t need = pred::rank_workspace_bytes(n_blocks, n_segments);
     if (need > 0 && (!workspace || ws_bytes < need))
-        return fail(PRED_ERR_WORKSPACE, "rank_victims needs a %zu-byte workspace (%zu given)", need,
+        return fail(PRED_ERR_WORKSPACE, "%s needs a %zu-byte workspace (%zu given)", what, need,
                     workspace ? ws_bytes : (size_t)0);
     if (need > 0 && ((uintptr_t)workspace & 7u)) return fail(PRED_ERR_WORKSPACE, "workspace must be 8-byte aligned");
-    hipError_t e = pred::launch_rank(scores, n_blocks, n_segments, victims, workspace, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "rank_victims launch");
+    hipError_t e = pred::launch_rank(scores, n_blocks, n_segments, k, victims, workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, what);
     return ok();
+}
+
+}  // namespace
+
+int pred_rank_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments, int32_t* victims,
+                      void* workspace, size_t ws_bytes, void* stream) {
+    return rank_or_select(p, scores, n_blocks, n_segments, n_blocks, victims, workspace, ws_bytes, stream,
+                          "rank_victims");
+}
+
+int pred_select_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments, int64_t k,
+                        int32_t* victims, void* workspace, size_t ws_bytes, void* stream) {
+    return rank_or_select(p, scores, n_blocks, n_segments, k, victims, workspace, ws_bytes, stream, "select_victims");
 }
 
 size_t pred_rank_workspace_bytes(int64_t n_blocks, int64_t n_segments) {

@@ -122,11 +122,13 @@ __device__ inline void bitonic_ks(uint64_t (&x)[4], uint64_t (*xb)[CH], int& lb,
     if constexpr (K < CH) bitonic_ks<CH, K * 2>(x, xb, lb, t);
 }
 
-// One workgroup per (segment, chunk) of up to CH keys.
+// One workgroup per (segment, chunk) of up to CH keys.  Only the first klim
+// places of each sorted chunk are written (klim = n for a full ranking); victims
+// rows are vstride apart.
 template <int CH>
 __global__ __launch_bounds__(CH / 4) void rank_bitonic_kernel(const float* __restrict__ scores, int64_t n,
-                                                              int64_t chunk_len, int nchunks,
-                                                              int32_t* __restrict__ victims,
+                                                              int64_t chunk_len, int nchunks, int64_t klim,
+                                                              int64_t vstride, int32_t* __restrict__ victims,
                                                               uint32_t* __restrict__ run_keys,
                                                               uint32_t* __restrict__ run_idx) {
     static_assert(CH >= 256 && CH <= 2048 && (CH & (CH - 1)) == 0, "one to eight waves of four keys per lane");
@@ -148,13 +150,13 @@ __global__ __launch_bounds__(CH / 4) void rank_bitonic_kernel(const float* __res
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int pos = 4 * t + e;
-        if (pos < len) {
-            const int64_t o = seg * n + off + pos;
+        if (pos < len && pos < klim) {
             if (run_keys) {
+                const int64_t o = seg * n + off + pos;
                 run_keys[o] = (uint32_t)(x[e] >> 32);
                 run_idx[o] = (uint32_t)x[e];
             } else {
-                victims[o] = (int32_t)(uint32_t)x[e];
+                victims[seg * vstride + off + pos] = (int32_t)(uint32_t)x[e];
             }
         }
     }
@@ -165,10 +167,17 @@ __global__ __launch_bounds__(CH / 4) void rank_bitonic_kernel(const float* __res
 // KiB for 8 runs of 1024, 128 KiB for 4 runs of 8192).  One workgroup places TPB
 // consecutive elements of one run; the output is the group sorted, as victims
 // when one group spans the segment, else as keys and indexes again.
+//
+// With klim < n (the k lowest only) a run's places from klim on are neither
+// placed nor counted: they are read as keys above every real one.  An element
+// among the k lowest has fewer than klim keys below it in any run, so its count
+// is unchanged; any other element still counts klim or more.  So the first
+// klim places come out exactly as in the full merge, and only they are written.
 template <int RL, int G, int TPB>
 __global__ __launch_bounds__(TPB) void rank_count_merge_kernel(const uint32_t* __restrict__ in_keys,
                                                                const uint32_t* __restrict__ in_idx, int64_t n,
-                                                               int nruns, int32_t* __restrict__ victims,
+                                                               int nruns, int64_t klim, int64_t vstride,
+                                                               int32_t* __restrict__ victims,
                                                                uint32_t* __restrict__ out_keys,
                                                                uint32_t* __restrict__ out_idx) {
     constexpr int GL = G * RL;       // keys of a full group
@@ -186,6 +195,10 @@ __global__ __launch_bounds__(TPB) void rank_count_merge_kernel(const uint32_t* _
     const int64_t g0 = (run0 / GL) * GL;                    // group start
     const int glen = (int)((n - g0) < GL ? (n - g0) : GL);
     const int own = (int)((run0 - g0) / RL);
+    const int kl = klim < RL ? (int)klim : RL;              // places of a run that can matter
+    const int rlen0 = (glen - own * RL) < RL ? (glen - own * RL) : RL;
+    const int rlen = rlen0 < kl ? rlen0 : kl;               // elements of its own run placed here
+    if (piece * TPB >= rlen) return;                         // whole workgroup: nothing to place
     const uint32_t* src = in_keys + seg * n + g0;
     {
         // the group's keys, padded to G full runs with a key above every real one
@@ -200,12 +213,11 @@ __global__ __launch_bounds__(TPB) void rank_count_merge_kernel(const uint32_t* _
 #pragma unroll
         for (int k = 0; k < L; ++k) {
             const int i = t + TPB * k;
-            gk[i] = i < glen ? v[k] : 0xFFFFFFFFu;
+            gk[i] = (i < glen && (i & (RL - 1)) < kl) ? v[k] : 0xFFFFFFFFu;
         }
     }
     __syncthreads();
 
-    const int rlen = (glen - own * RL) < RL ? (glen - own * RL) : RL;
     const int i = piece * TPB + t;                           // this thread's element of its run
     const uint32_t x = gk[own * RL + (i < rlen ? i : 0)];
     int pos = i;                                             // the elements of its own run before it
@@ -221,14 +233,13 @@ __global__ __launch_bounds__(TPB) void rank_count_merge_kernel(const uint32_t* _
         lo += a[lo] < xr ? 1 : 0;                            // lo <= RL - 1 before this
         pos += r == own ? 0 : lo;
     }
-    if (i < rlen && pos < glen) {   // pos < glen always holds; never write outside the group
-        const int64_t dst = seg * n + g0 + pos;
+    if (i < rlen && pos < glen && pos < klim) {   // pos < glen always holds; never write outside the group
         const uint32_t id = in_idx[seg * n + run0 + i];
         if (g0 == 0 && glen == n) {
-            victims[dst] = (int32_t)id;
+            victims[seg * vstride + pos] = (int32_t)id;
         } else {
-            out_keys[dst] = x;
-            out_idx[dst] = id;
+            out_keys[seg * n + g0 + pos] = x;
+            out_idx[seg * n + g0 + pos] = id;
         }
     }
 }
@@ -236,13 +247,15 @@ __global__ __launch_bounds__(TPB) void rank_count_merge_kernel(const uint32_t* _
 // Rows over 32768 keys: merge sorted runs [base, base+run) and [base+run,
 // base+2run) of every segment.  An element counts the other run's keys before
 // it by binary search: keys below it, and for the first run (lower indexes)
-// also keys equal to it.
+// also keys equal to it.  With klim < n only each run's first klim places take
+// part (the same argument as for the counting merge).
 __global__ __launch_bounds__(256) void rank_merge_kernel(const uint32_t* __restrict__ in_keys,
                                                          const uint32_t* __restrict__ in_idx,
                                                          uint32_t* __restrict__ out_keys,
                                                          uint32_t* __restrict__ out_idx,
                                                          int32_t* __restrict__ victims, int64_t n,
-                                                         int64_t n_seg, int64_t run) {
+                                                         int64_t n_seg, int64_t run, int64_t klim,
+                                                         int64_t vstride) {
     const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (gi >= n * n_seg) return;
     const int64_t seg = gi / n;
@@ -259,25 +272,28 @@ __global__ __launch_bounds__(256) void rank_merge_kernel(const uint32_t* __restr
     } else {            // keys of the first run at most x
         lo = base; hi = a_end; mine = pos - a_end; xr = x + 1u;
     }
+    if (mine >= klim) return;
+    if (hi - lo > klim) hi = lo + klim;
     const int64_t first = lo;
     while (lo < hi) {
         const int64_t mid = lo + ((hi - lo) >> 1);
         if (row[mid] < xr) lo = mid + 1;
         else hi = mid;
     }
-    const int64_t dst = seg * n + base + mine + (lo - first);
+    const int64_t place = mine + (lo - first);               // in the merged run starting at base
+    if (place >= klim) return;
     const uint32_t id = in_idx[seg * n + pos];
     if (victims) {
-        victims[dst] = (int32_t)id;
+        victims[seg * vstride + base + place] = (int32_t)id;   // base is 0 in the last merge
     } else {
-        out_keys[dst] = x;
-        out_idx[dst] = id;
+        out_keys[seg * n + base + place] = x;
+        out_idx[seg * n + base + place] = id;
     }
 }
 
 template <int RL, int G, int TPB>
-hipError_t launch_count_merge(const uint32_t* ik, const uint32_t* ii, int64_t n, int64_t n_seg, int32_t* victims,
-                              uint32_t* ok, uint32_t* oi, hipStream_t st) {
+hipError_t launch_count_merge(const uint32_t* ik, const uint32_t* ii, int64_t n, int64_t n_seg, int64_t klim,
+                              int64_t vstride, int32_t* victims, uint32_t* ok, uint32_t* oi, hipStream_t st) {
     const int nruns = (int)((n + RL - 1) / RL);
     const size_t lds = (size_t)G * RL * sizeof(uint32_t);
     if (lds > 65536) {
@@ -286,7 +302,7 @@ hipError_t launch_count_merge(const uint32_t* ik, const uint32_t* ii, int64_t n,
         if (e != hipSuccess) return e;
     }
     rank_count_merge_kernel<RL, G, TPB><<<(unsigned)(n_seg * nruns * (RL / TPB)), TPB, lds, st>>>(
-        ik, ii, n, nruns, victims, ok, oi);
+        ik, ii, n, nruns, klim, vstride, victims, ok, oi);
     return hipGetLastError();
 }
 
@@ -298,7 +314,7 @@ size_t rank_workspace_bytes(int64_t n, int64_t n_seg) {
     return (size_t)((n <= kMaxLdsItems ? 1 : 2) * n * n_seg) * sizeof(uint64_t);
 }
 
-hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int32_t* victims, void* ws,
+hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int64_t k, int32_t* victims, void* ws,
                        hipStream_t st) {
     if (n <= 0 || n_seg <= 0) return hipSuccess;
     // largest grids of the path this row length takes: the step-1 sort, the
@@ -308,15 +324,15 @@ hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int32_t* v
         !grid_fits((n * n_seg + 255) / 256))
         return hipErrorInvalidConfiguration;
     if (n <= 256) {
-        rank_bitonic_kernel<256><<<(unsigned)n_seg, 64, 0, st>>>(scores, n, n, 1, victims, nullptr, nullptr);
+        rank_bitonic_kernel<256><<<(unsigned)n_seg, 64, 0, st>>>(scores, n, n, 1, k, k, victims, nullptr, nullptr);
         return hipGetLastError();
     }
     if (n <= 1024) {
-        rank_bitonic_kernel<1024><<<(unsigned)n_seg, 256, 0, st>>>(scores, n, n, 1, victims, nullptr, nullptr);
+        rank_bitonic_kernel<1024><<<(unsigned)n_seg, 256, 0, st>>>(scores, n, n, 1, k, k, victims, nullptr, nullptr);
         return hipGetLastError();
     }
     if (n <= kSingle) {
-        rank_bitonic_kernel<2048><<<(unsigned)n_seg, 512, 0, st>>>(scores, n, n, 1, victims, nullptr, nullptr);
+        rank_bitonic_kernel<2048><<<(unsigned)n_seg, 512, 0, st>>>(scores, n, n, 1, k, k, victims, nullptr, nullptr);
         return hipGetLastError();
     }
     // workspace: buffer A = run keys then run indexes (4 + 4 bytes per key), and
@@ -327,22 +343,23 @@ hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int32_t* v
     uint32_t* bk = ai + total;
     uint32_t* bi = bk + total;
     const int nruns = (int)((n + kChunk - 1) / kChunk);
-    rank_bitonic_kernel<kChunk><<<(unsigned)(n_seg * nruns), kChunk / 4, 0, st>>>(scores, n, kChunk, nruns, nullptr,
-                                                                                ak, ai);
+    rank_bitonic_kernel<kChunk><<<(unsigned)(n_seg * nruns), kChunk / 4, 0, st>>>(scores, n, kChunk, nruns, k, k,
+                                                                                nullptr, ak, ai);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // runs of 1024 -> groups of 8192 (the whole row when it is no longer)
-    e = launch_count_merge<kChunk, kMaxLdsItems / kChunk, kMergeTPB>(ak, ai, n, n_seg, victims, bk, bi, st);
+    e = launch_count_merge<kChunk, kMaxLdsItems / kChunk, kMergeTPB>(ak, ai, n, n_seg, k, k, victims, bk, bi, st);
     if (e != hipSuccess || n <= kMaxLdsItems) return e;
     // runs of 8192 -> groups of 32768 (128 KiB of keys in LDS)
-    e = launch_count_merge<kMaxLdsItems, kMaxGroup2 / kMaxLdsItems, kMergeTPB>(bk, bi, n, n_seg, victims, ak, ai, st);
+    e = launch_count_merge<kMaxLdsItems, kMaxGroup2 / kMaxLdsItems, kMergeTPB>(bk, bi, n, n_seg, k, k, victims, ak,
+                                                                               ai, st);
     if (e != hipSuccess || n <= kMaxGroup2) return e;
     // longer rows: pairwise merges of runs of 32768, 65536, ...
     uint32_t *ik = ak, *ii = ai, *ok = bk, *oi = bi;
     const unsigned grid = (unsigned)((total + 255) / 256);
     for (int64_t run = kMaxGroup2; run < n; run *= 2) {
         const bool last = 2 * run >= n;
-        rank_merge_kernel<<<grid, 256, 0, st>>>(ik, ii, ok, oi, last ? victims : nullptr, n, n_seg, run);
+        rank_merge_kernel<<<grid, 256, 0, st>>>(ik, ii, ok, oi, last ? victims : nullptr, n, n_seg, run, k, k);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         uint32_t* tk = ik; ik = ok; ok = tk;

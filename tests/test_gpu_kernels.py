@@ -245,6 +245,36 @@ def test_rank_special_orders(kind):
     assert np.array_equal(got, predictor.rank_victims(s))
 
 
+@pytest.mark.parametrize("n,segs,ks", [(200, 3, (1, 7, 199, 200)), (1000, 2, (1, 64, 999)), (2048, 2, (1, 1024, 2047)),
+                                       (5000, 3, (1, 64, 1023, 1024, 1025, 4999)), (8192, 2, (1, 100, 8192)),
+                                       (20000, 1, (1, 64, 1024, 8191, 8192, 8193, 19999)),
+                                       (40000, 1, (1, 777, 32768, 39999))])
+def test_select_exact(n, segs, ks):
+    """pred_select_victims: exactly the first k of the full ranking, on every path (one workgroup,
+    chunked with one or two counting-merge levels, pairwise merges)."""
+    rng = np.random.default_rng(n + 31 * segs)
+    s = (rng.integers(-200, 200, size=(segs, n)) * 0.5).astype(np.float32)   # many ties
+    s[:, :: 53] = -0.0
+    s[0, 2] = np.nan
+    s[-1, -1] = -np.inf
+    want_all = predictor.rank_victims(s)
+    d = rk.dims(1, 1, 1, 8, 8, 1, 1)
+    with rk.Predictor(d, 1) as p:
+        sc = torch.from_numpy(s).cuda()
+        ws_b = rk.pred_rank_workspace_bytes(n, segs)
+        ws = torch.empty((ws_b // 8 + 1,), dtype=torch.int64, device="cuda") if ws_b else None
+        for k in ks:
+            _say("select", n, segs, k)
+            vic = torch.full((segs, k), -7, dtype=torch.int32, device="cuda")
+            rk.pred_select_victims(p.handle, sc, k, vic, ws)
+            got = vic.cpu().numpy()
+            assert np.array_equal(got, want_all[:, :k]), (n, segs, k)
+        with pytest.raises(rk.PredError) as e:
+            rk.pred_select_victims(p.handle, sc, n + 1, torch.empty((segs, n + 1), dtype=torch.int32, device="cuda"), ws)
+        assert e.value.code == rk.PRED_ERR_OUT_OF_RANGE
+        rk.pred_select_victims(p.handle, sc, 0, torch.empty((segs, 0), dtype=torch.int32, device="cuda"), ws)
+
+
 def test_rank_requires_workspace():
     d = rk.dims(1, 1, 1, 8, 8, 1, 1)
     with rk.Predictor(d, 1) as p:

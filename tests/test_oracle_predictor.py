@@ -311,3 +311,20 @@ def test_order_key_monotone():
     assert np.all(np.diff(np.delete(keys, 3)) > 0)
     assert predictor.order_key(np.array([np.nan], np.float32))[0] == 0
     assert keys.min() > 0
+
+
+def test_select_is_the_sorted_prefix():
+    """select_victims against Python's sorted() truncated to k, on rows with many ties, -0, NaN and inf."""
+    rng = np.random.default_rng(13)
+    for n in [1, 5, 64, 300]:
+        s = rng.integers(-4, 5, size=(2, n)).astype(np.float32) * 0.25
+        s[0, :: max(1, n // 5)] = -0.0
+        s[1, :: max(1, n // 7)] = np.nan
+        s[1, -1] = -np.inf
+        for k in sorted({0, 1, n // 2, n - 1, n} - {-1}):
+            got = predictor.select_victims(s, k)
+            assert got.shape == (2, k)
+            for row in range(2):
+                vals = [float(v) for v in s[row]]
+                want = sorted(range(n), key=lambda b: (_key_py(vals[b]), b))[:k]
+                assert got[row].tolist() == want
