@@ -177,6 +177,45 @@ int pred_rank_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t 
 int pred_select_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments, int64_t k,
                         int32_t* victims, void* workspace, size_t ws_bytes, void* stream);
 
+/* Per-row causal block scores of a prefill chunk (qsa_select.rs page, prefill
+ * selection: each query row is scored against the blocks complete at its
+ * position; the score is the predictor's, predictor.rs page, score_blocks, kept
+ * per row instead of maximised over rows).
+ *   layer        A_g layer to read, 0 <= layer < num_layers
+ *   q_proj       device, [rows, num_q_heads, r] bf16; row i sits at position
+ *                first_pos + i of the sequence
+ *   block_table  device, [n_blocks] int32 physical ids of the sequence's
+ *                blocks, or NULL for slots 0..n_blocks-1
+ *   scores       device, [rows, stride] float32 output
+ * With complete(i) = min(n_blocks, (first_pos + i + 1) / block_size), the
+ * blocks whose every token is at or before row i's position:
+ *   scores[i, b] = max over query heads h, tokens t of
+ *                  sum_j q_proj[i, h, j] * A_g[layer, table[b], h / g, t, j]
+ * for b < complete(i) (float32 accumulation, no scale), and -inf for
+ * complete(i) <= b < stride.  A table entry outside [0, max_blocks) gives a
+ * complete block a NaN score and raises the device error word.  rows and
+ * n_blocks <= 2^31-1; rows * stride == 0 is a no-op; q_proj must be 16-byte
+ * aligned. */
+int pred_score_rows(pred_t* p, int32_t layer, const pred_bf16* q_proj, int64_t rows, int64_t first_pos,
+                    const int32_t* block_table, int64_t n_blocks, float* scores, int64_t stride,
+                    void* stream);
+
+/* Per-row keep sets (qsa_select.rs page, prefill selection's top-k per row,
+ * here on the device): for row i the first c(i) = min(stride,
+ * (first_pos + i + 1) / ratio) entries of scores row i, ordered by descending
+ * score with equal scores in ascending index order (-0 equal to +0, NaN after
+ * everything), and the first topk of them written to keep row i.  Slots past
+ * c(i) hold -1.
+ *   scores     device, [rows, stride] float32 (e.g. pred_score_rows's output,
+ *              with ratio = block_size)
+ *   keep       device, [rows, topk] int32 output
+ *   ratio      >= 1; first_pos in [0, 2^62]; 0 <= topk <= stride
+ *   workspace  pred_rank_workspace_bytes(stride, rows) bytes (NULL when 0)
+ * rows and stride must be <= 2^31-1. */
+int pred_select_keep(pred_t* p, const float* scores, int64_t rows, int64_t stride, int64_t first_pos,
+                     int32_t ratio, int64_t topk, int32_t* keep, void* workspace, size_t ws_bytes,
+                     void* stream);
+
 /* Workspace pred_rank_victims needs for this shape: 0 for n_blocks <= 2048
  * (each segment is sorted inside one workgroup), else 8 bytes per key for the
  * sorted runs, twice that for n_blocks > 8192 (pairwise merge buffers). */

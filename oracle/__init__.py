@@ -26,6 +26,11 @@ Parity status per function (what pins it is listed in each module docstring):
 * ``predictor.rank_victims``                        pinned (sorted() on tiny inputs,
                                                     permutation validity, planted blocks)
 * ``predictor.select_victims``                      pinned (sorted() truncated to k)
+* ``predictor.score_rows``                          pinned (pure-Python brute force per cell,
+                                                    max over rows equals score_blocks,
+                                                    causal mask by hand)
+* ``predictor.keep_sets``                           pinned (sorted() with the page's
+                                                    comparator, hand-worked example)
 """
 
 from . import bf16, prng, predictor  # noqa: F401

@@ -21,7 +21,12 @@ Readings where the pages leave a step open:
   block table (an absent table is the identity, which is the pages' contiguous
   ``k_lr_seq`` case); ties rank the lower logical index first;
 * every one of a block's B tokens is scored (no fill length is passed);
-* ranking key: -0 is +0, every NaN ranks first.
+* ranking key: -0 is +0, every NaN ranks first;
+* per-row keep sets (the qsa_select.rs page's prefill selection, rebuilt on the
+  predictor's score): a row at position p sees blocks ``b < (p + 1) // B`` (the
+  block size is the page's ratio), scores the rest -inf, keeps the top-k by
+  descending score with the lower index first on ties; NaN goes last, and a row
+  with fewer than k complete blocks pads its list with -1.
 """
 
 import numpy as np
@@ -153,3 +158,67 @@ def select_victims(scores, k):
     first k entries of ``rank_victims`` (the predictor page's module doc: scores only
     rank eviction victims; a cache evicts a few blocks at a time)."""
     return rank_victims(scores)[:, :k]
+
+
+# ------------------------------------------------- per-row causal keep sets
+
+def complete_blocks(first_pos, row, ratio, limit):
+    """Blocks complete at position ``first_pos + row``: ``(first_pos + row + 1) // ratio``,
+    at most ``limit`` (the qsa_select.rs page's per-row count in its prefill selection)."""
+    return min(limit, (first_pos + row + 1) // ratio)
+
+
+def score_rows(q_rows, slots, first_pos, stride):
+    """Per-row causal block scores of one layer and sequence, float64.
+
+    ``q_rows [rows, Hq, R]`` bf16, row i at position ``first_pos + i``; ``slots
+    [n, Hk, B, R]`` bf16 low-rank keys of the sequence's blocks in logical order.
+    Returns ``[rows, stride]``: for ``b < complete(i) = min(n, (first_pos + i + 1) // B)``
+    the predictor's score of block b for row i alone (max over query heads h and
+    tokens t of ``q[i, h] . A[b, h // g, t]``), and -inf for the other columns
+    (qsa_select.rs page: each row sees only the blocks complete at its position;
+    the block size plays the page's ratio).
+    """
+    q = bf16.decode(q_rows)
+    rows, Hq, R = q.shape
+    n, Hk, B, _ = slots.shape
+    g = Hq // Hk
+    best = np.full((rows, n), -np.inf)
+    chunk = max(1, min(n, (1 << 24) // max(1, rows * B)))   # logits of at most 2^24 entries
+    for b0 in range(0, n, chunk):
+        a = bf16.decode(slots[b0:b0 + chunk])                # [c, Hk, B, R]
+        c = a.shape[0]
+        for h in range(Hq):
+            ak = a[:, h // g].reshape(c * B, R)
+            logits = q[:, h, :] @ ak.T                       # [rows, c*B]
+            per_block = logits.reshape(rows, c, B).max(axis=2)
+            best[:, b0:b0 + c] = np.maximum(best[:, b0:b0 + c], per_block)
+    out = np.full((rows, stride), -np.inf)
+    for i in range(rows):
+        c = complete_blocks(first_pos, i, B, min(n, stride))
+        out[i, :c] = best[i, :c]
+    return out
+
+
+def keep_sets(scores_f32, first_pos, ratio, topk):
+    """Per-row keep lists (qsa_select.rs page, prefill selection's host top-k).
+
+    For row i of ``scores [rows, stride]`` (float32) the first
+    ``complete(i) = min(stride, (first_pos + i + 1) // ratio)`` scores are ordered
+    larger first, equal scores by lower index; the first ``topk`` indices are the
+    row's keep list, and slots past ``complete(i)`` hold -1.  -0 equals +0; NaN
+    (which the page's comparator leaves unordered) goes after every number.
+    Returns int32 ``[rows, topk]``.
+    """
+    s = np.atleast_2d(np.asarray(scores_f32, dtype=np.float32))
+    rows, stride = s.shape
+    out = np.full((rows, topk), -1, np.int32)
+    for i in range(rows):
+        c = complete_blocks(first_pos, i, ratio, stride)
+        v = s[i, :c].astype(np.float64)
+        nan = np.isnan(v)
+        neg = np.where(nan, 0.0, -v) + 0.0                   # descending; -0 and +0 become one key
+        order = np.lexsort((np.arange(c), neg, nan))         # last key is the primary one
+        m = min(topk, c)
+        out[i, :m] = order[:m]
+    return out

@@ -192,6 +192,36 @@ def pred_select_victims(h, scores, k, victims, workspace=None, stream=None):
                                      ws_bytes, _stream(stream)))
 
 
+def pred_score_rows(h, layer, q_proj, first_pos, block_table, n_blocks, scores, stream=None):
+    """Per-row causal scores: q_proj [rows, Hq, R] bf16 (row i at position first_pos + i);
+    block_table [n_blocks] int32 or None; scores [rows, stride] float32."""
+    import torch
+    d = pred_get_dims(h)
+    if q_proj.dim() != 3 or tuple(q_proj.shape[1:]) != (d.num_q_heads, d.r):
+        raise ValueError(f"q_proj must be [rows, {d.num_q_heads}, {d.r}]")
+    rows = q_proj.shape[0]
+    if scores.dim() != 2 or scores.shape[0] != rows:
+        raise ValueError("scores must be [rows, stride]")
+    if block_table is not None and tuple(block_table.shape) != (n_blocks,):
+        raise ValueError("block_table must be [n_blocks]")
+    _check(lib().pred_score_rows(h, layer, _ptr(q_proj, "q_proj", _bf16_types()), rows, first_pos,
+                                 _ptr(block_table, "block_table", (torch.int32,)), n_blocks,
+                                 _ptr(scores, "scores", (torch.float32,)), scores.shape[1], _stream(stream)))
+
+
+def pred_select_keep(h, scores, first_pos, ratio, topk, keep, workspace=None, stream=None):
+    """scores [rows, stride] float32 -> keep [rows, topk] int32: per row, the top-k of the blocks complete
+    at its position (descending, lower index on ties, -1 past the complete ones)."""
+    import torch
+    if scores.dim() != 2 or keep.dim() != 2 or keep.shape[0] != scores.shape[0] or keep.shape[1] != topk:
+        raise ValueError("scores must be [rows, stride] and keep [rows, topk]")
+    rows, stride = scores.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pred_select_keep(h, _ptr(scores, "scores", (torch.float32,)), rows, stride, first_pos, ratio,
+                                  topk, _ptr(keep, "keep", (torch.int32,)), _ptr(workspace, "workspace"),
+                                  ws_bytes, _stream(stream)))
+
+
 # ------------------------------------------------------------------ inspection
 
 def pred_copy_projection(h):

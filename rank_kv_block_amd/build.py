@@ -20,7 +20,8 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
-SOURCES = ["pred_api.hip", "proj.hip", "score_decode.hip", "score_prefill.hip", "rank.hip", "prng.cpp"]
+SOURCES = ["pred_api.hip", "proj.hip", "score_decode.hip", "score_prefill.hip", "score_rows.hip", "rank.hip",
+           "prng.cpp"]
 # the projection generator must be plain IEEE float64 arithmetic, one operation at a time
 EXTRA = {
     "prng.cpp": ["-ffp-contract=off", "-fno-fast-math"],

@@ -66,6 +66,31 @@ __device__ inline uint32_t order_key(float x) {
     return (u & 0x80000000u) ? ~u : (u ^ 0x80000000u);
 }
 
+// MFMA operand and accumulator types (v_mfma_f32_32x32x16_bf16).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// 16 bytes as a plain vector (uint4 is a union-based struct, which keeps arrays
+// of it from being split into registers)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Eight bf16 from 16 aligned bytes.
+__device__ inline bf16x8_t load8(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
+}
+
+// A float from another lane: M = 1, 2 swap neighbours and pairs (DPP quad
+// permutes); M = 7 and 15 mirror within 8 and 16 lanes (DPP row half-mirror and
+// mirror: after the quads agree, one step combines the two quads or the two
+// halves); other M through ds_swizzle / ds_bpermute.
+template <int M>
+__device__ inline float lane_xor(float v) {
+    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+    if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+    if constexpr (M == 7) return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
+    if constexpr (M == 15) return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true));
+    return __shfl_xor(v, M);
+}
+
 __device__ inline float key_to_float(uint32_t k) {
     if (k == 0u) return __uint_as_float(0x7FC00000u);
     return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace pred {
 
 // A launch takes at most 2^31 - 1 workgroups; a call that would need more is
@@ -35,9 +37,48 @@ struct ScoreArgs {
 hipError_t launch_score_decode_or_generic(const ScoreArgs& a, hipStream_t stream);
 const char* score_decode_path_name(const ScoreArgs& a);
 
+// ---- per-row causal scores (score_rows.hip) --------------------------------
+struct RowScoreArgs {
+    const uint16_t* qp;     // [rows, Hq, R]; row r sits at position first_pos + r
+    const uint16_t* ag;     // A_g base [L, N, Hk, B, R]
+    const int32_t* table;   // [n] physical ids, or null for slots 0..n-1
+    float* scores;          // [rows, stride]
+    uint32_t* err;
+    int64_t N;              // max_blocks
+    int64_t layer;
+    int64_t n;              // blocks of the sequence (table entries)
+    int64_t rows, first_pos, stride;
+    int Hq, Hk, B, R;
+};
+// Blocks complete at the position of row r: min(n, (first_pos + r + 1) / B).
+hipError_t launch_score_rows(const RowScoreArgs& a, hipStream_t stream);
+const char* score_rows_path_name(const RowScoreArgs& a);
+
 // ---- ranking (rank.hip) --------------------------------------------------
 size_t rank_workspace_bytes(int64_t n, int64_t n_seg);
-hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int64_t k, int32_t* victims, void* ws,
-                       hipStream_t stream);
+// Sort order of a ranking row.  Ascending (eviction order): the order key of
+// the score, NaN first.  Descending (a keep set, larger score first): keys
+// flipped inside [0, 0xFF800001] so that they stay below the padding key and
+// key + 1 never overflows; NaN last.  Ties always go to the lower index.
+// With ratio > 0 only the first min(n, (first_pos + row + 1) / ratio) entries
+// of row `row` take part (the blocks complete at that row's position).
+struct RowOrder {
+    int desc;
+    int64_t first_pos;
+    int32_t ratio;
+
+    __device__ inline uint32_t key(float v) const {
+        if (!desc) return order_key(v);
+        return v != v ? 0xFF800001u : 0xFF800000u - order_key(v);
+    }
+    __host__ __device__ inline int64_t row_len(int64_t row, int64_t n) const {
+        if (ratio <= 0) return n;
+        const int64_t c = (first_pos + row + 1) / ratio;
+        return c < n ? c : n;
+    }
+};
+
+hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int64_t k, RowOrder ro, int32_t* victims,
+                       void* ws, hipStream_t stream);
 
 }  // namespace pred

@@ -184,7 +184,9 @@ const char* pred_limits(void) {
     return "head_dim and r multiples of 8; r <= 256; head_dim <= 65536; 16-byte aligned q, q_proj and k "
            "buffers. Streaming decode scorer: r in {16,32,64,128} and block_size*r/8 a power of two <= 1024; "
            "other shapes use a plain per-block kernel. Rank: n_blocks <= 2^31-1; above 2048 per segment a "
-           "workspace of 8*n_blocks*n_segments bytes is needed (16*n_blocks*n_segments above 8192).";
+           "workspace of 8*n_blocks*n_segments bytes is needed (16*n_blocks*n_segments above 8192); select_keep "
+           "the same with n_blocks = stride, n_segments = rows. Row scorer: MFMA for r in {16,32,64,128}, "
+           "block_size in {8,16,32}, num_kv_heads in {1,2,4,8}, num_kv_heads*r <= 512; a plain kernel otherwise.";
 }
 
 const char* pred_version(void) { return "rank_kv_block_amd 0.1 (gfx950)"; }
@@ -288,11 +290,51 @@ int pred_score_blocks(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf
     return ok();
 }
 
+int pred_score_rows(pred_t* p, int32_t layer, const pred_bf16* q_proj, int64_t rows, int64_t first_pos,
+                    const int32_t* block_table, int64_t n_blocks, float* scores, int64_t stride, void* stream) {
+    if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
+    if (layer < 0 || layer >= p->d.num_layers)
+        return fail(PRED_ERR_OUT_OF_RANGE, "score_rows: layer %d outside [0, %d)", layer, p->d.num_layers);
+    if (rows < 0 || first_pos < 0 || n_blocks < 0 || stride < 0)
+        return fail(PRED_ERR_OUT_OF_RANGE, "negative count (rows %lld, first_pos %lld, n_blocks %lld, stride %lld)",
+                    (long long)rows, (long long)first_pos, (long long)n_blocks, (long long)stride);
+    if (rows > 2147483647LL || first_pos > (1LL << 62) || n_blocks > 2147483647LL)
+        return fail(PRED_ERR_OUT_OF_RANGE, "score_rows: rows and n_blocks must be <= 2^31-1, first_pos <= 2^62");
+    if (!block_table && n_blocks > p->d.max_blocks)
+        return fail(PRED_ERR_OUT_OF_RANGE, "score_rows: %lld blocks without a table, max_blocks %lld",
+                    (long long)n_blocks, (long long)p->d.max_blocks);
+    int64_t cells;
+    if (!mul_ok(rows, stride, &cells)) return fail(PRED_ERR_OUT_OF_RANGE, "rows * stride too large");
+    if (cells == 0) return ok();
+    if (!q_proj || !scores) return fail(PRED_ERR_NULL_ARG, "q_proj or scores is NULL");
+    if (!aligned16(q_proj)) return fail(PRED_ERR_UNSUPPORTED, "q_proj must be 16-byte aligned");
+    pred::RowScoreArgs a;
+    a.qp = q_proj;
+    a.ag = p->ag_dev;
+    a.table = block_table;
+    a.scores = scores;
+    a.err = p->err_dev;
+    a.N = p->d.max_blocks;
+    a.layer = layer;
+    a.n = n_blocks;
+    a.rows = rows;
+    a.first_pos = first_pos;
+    a.stride = stride;
+    a.Hq = p->d.num_q_heads;
+    a.Hk = p->d.num_kv_heads;
+    a.B = p->d.block_size;
+    a.R = p->d.r;
+    hipError_t e = pred::launch_score_rows(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "score_rows launch");
+    return ok();
+}
+
 namespace {
 
 // The k lowest of every segment, in eviction order; k = n_blocks is the full ranking.
-int rank_or_select(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments, int64_t k, int32_t* victims,
-                   void* workspace, size_t ws_bytes, void* stream, const char* what) {
+int rank_or_select(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments, int64_t k,
+                   pred::RowOrder ro, int32_t* victims, void* workspace, size_t ws_bytes, void* stream,
+                   const char* what) {
     if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
     if (n_blocks < 0 || n_segments < 0)
         return fail(PRED_ERR_OUT_OF_RANGE, "negative count (n_blocks %lld, n_segments %lld)", (long long)n_blocks,
@@ -308,7 +350,7 @@ int rank_or_select(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_s
         return fail(PRED_ERR_WORKSPACE, "%s needs a %zu-byte workspace (%zu given)", what, need,
                     workspace ? ws_bytes : (size_t)0);
     if (need > 0 && ((uintptr_t)workspace & 7u)) return fail(PRED_ERR_WORKSPACE, "workspace must be 8-byte aligned");
-    hipError_t e = pred::launch_rank(scores, n_blocks, n_segments, k, victims, workspace, (hipStream_t)stream);
+    hipError_t e = pred::launch_rank(scores, n_blocks, n_segments, k, ro, victims, workspace, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, what);
     return ok();
 }
@@ -317,13 +359,24 @@ int rank_or_select(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_s
 
 int pred_rank_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments, int32_t* victims,
                       void* workspace, size_t ws_bytes, void* stream) {
-    return rank_or_select(p, scores, n_blocks, n_segments, n_blocks, victims, workspace, ws_bytes, stream,
-                          "rank_victims");
+    return rank_or_select(p, scores, n_blocks, n_segments, n_blocks, pred::RowOrder{0, 0, 0}, victims, workspace,
+                          ws_bytes, stream, "rank_victims");
 }
 
 int pred_select_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments, int64_t k,
                         int32_t* victims, void* workspace, size_t ws_bytes, void* stream) {
-    return rank_or_select(p, scores, n_blocks, n_segments, k, victims, workspace, ws_bytes, stream, "select_victims");
+    return rank_or_select(p, scores, n_blocks, n_segments, k, pred::RowOrder{0, 0, 0}, victims, workspace, ws_bytes,
+                          stream, "select_victims");
+}
+
+int pred_select_keep(pred_t* p, const float* scores, int64_t rows, int64_t stride, int64_t first_pos, int32_t ratio,
+                     int64_t topk, int32_t* keep, void* workspace, size_t ws_bytes, void* stream) {
+    if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
+    if (ratio < 1) return fail(PRED_ERR_OUT_OF_RANGE, "ratio (%d) must be >= 1", ratio);
+    if (first_pos < 0 || first_pos > (1LL << 62))
+        return fail(PRED_ERR_OUT_OF_RANGE, "first_pos (%lld) outside [0, 2^62]", (long long)first_pos);
+    return rank_or_select(p, scores, stride, rows, topk, pred::RowOrder{1, first_pos, ratio}, keep, workspace,
+                          ws_bytes, stream, "select_keep");
 }
 
 size_t pred_rank_workspace_bytes(int64_t n_blocks, int64_t n_segments) {

@@ -24,6 +24,13 @@
 //      of 8192 (128 KiB of keys in LDS); rows over 32768 then merge runs
 //      pairwise, each element finding its place by binary search in the other
 //      run.
+//
+// The same machinery gives a per-row keep set (qsa_select.rs page, host top-k
+// of a prefill chunk): descending order keys (larger score first, ties still to
+// the lower index) and, per row, only the blocks complete at that row's
+// position.  A row's other entries enter as padding keys above every real key;
+// the merges place padding like equal keys and carry index -1 for it, so the
+// slots of a row with fewer eligible blocks than asked for come out as -1.
 #include "common.h"
 #include "kernels.h"
 
@@ -35,6 +42,7 @@ constexpr int kMaxLdsItems = 8192;   // keys of one step-2 group, merged in LDS
 constexpr int kChunk = 1024;         // keys per sorted run of step 1 (measured best of 512 / 1024 / 2048)
 constexpr int kSingle = 2048;        // up to this many keys a segment is sorted by one workgroup
 constexpr int kMergeTPB = 1024;      // step-2 threads per workgroup (one key of its run each)
+constexpr uint32_t kPadKey = 0xFFFFFFFFu;   // padding: above every sort key
 constexpr int kMaxGroup2 = 32768;    // keys of one second-level group (128 KiB of LDS)
 
 // Sorting network for one chunk of CH keys (power of two, 256..2048), 4 per
@@ -128,7 +136,8 @@ __device__ inline void bitonic_ks(uint64_t (&x)[4], uint64_t (*xb)[CH], int& lb,
 template <int CH>
 __global__ __launch_bounds__(CH / 4) void rank_bitonic_kernel(const float* __restrict__ scores, int64_t n,
                                                               int64_t chunk_len, int nchunks, int64_t klim,
-                                                              int64_t vstride, int32_t* __restrict__ victims,
+                                                              int64_t vstride, RowOrder ro,
+                                                              int32_t* __restrict__ victims,
                                                               uint32_t* __restrict__ run_keys,
                                                               uint32_t* __restrict__ run_idx) {
     static_assert(CH >= 256 && CH <= 2048 && (CH & (CH - 1)) == 0, "one to eight waves of four keys per lane");
@@ -138,12 +147,14 @@ __global__ __launch_bounds__(CH / 4) void rank_bitonic_kernel(const float* __res
     const int64_t off = (int64_t)(blockIdx.x % nchunks) * chunk_len;
     const int len = (int)((n - off) < chunk_len ? (n - off) : chunk_len);
     const float* src = scores + seg * n + off;
+    const int64_t valid = ro.row_len(seg, n);   // entries of this row that take part
     uint64_t x[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int pos = 4 * t + e;
-        // padding sorts after every real key (key 0xFFFFFFFF is above the key of +inf)
-        x[e] = pos < len ? (((uint64_t)order_key(src[pos]) << 32) | (uint32_t)(off + pos)) : ~0ull;
+        // padding sorts after every real key (sort keys stay below kPadKey)
+        x[e] = (pos < len && off + pos < valid) ? (((uint64_t)ro.key(src[pos]) << 32) | (uint32_t)(off + pos))
+                                                : ~0ull;
     }
     int lb = 0;
     bitonic_ks<CH, 2>(x, xb, lb, t);
@@ -220,20 +231,24 @@ __global__ __launch_bounds__(TPB) void rank_count_merge_kernel(const uint32_t* _
 
     const int i = piece * TPB + t;                           // this thread's element of its run
     const uint32_t x = gk[own * RL + (i < rlen ? i : 0)];
+    const bool pad = x == kPadKey;                           // a row's entries past its eligible count
     int pos = i;                                             // the elements of its own run before it
     // every run is searched (the own run too, its count discarded): no branch, so
     // the G searches are independent chains of LDS reads that interleave
 #pragma unroll
     for (int r = 0; r < G; ++r) {
         const uint32_t xr = x + (r < own ? 1u : 0u);         // earlier run: equal keys count as well
-        const uint32_t* a = gk + r * RL;                     // (no overflow: x <= order key of +inf)
+        const uint32_t* a = gk + r * RL;                     // (x + 1 wraps only for padding, not used then)
         int lo = 0;
 #pragma unroll
         for (int step = RL / 2; step >= 1; step >>= 1) lo += a[lo + step - 1] < xr ? step : 0;
         lo += a[lo] < xr ? 1 : 0;                            // lo <= RL - 1 before this
-        pos += r == own ? 0 : lo;
+        // padding is placed as a key equal to the other padding: all of an
+        // earlier run (a whole run of RL) comes before it, and a later run's
+        // real keys; it carries index -1 to the output
+        pos += r == own ? 0 : ((pad && r < own) ? RL : lo);
     }
-    if (i < rlen && pos < glen && pos < klim) {   // pos < glen always holds; never write outside the group
+    if (i < rlen && pos < glen && pos < klim) {             // pos < glen always holds
         const uint32_t id = in_idx[seg * n + run0 + i];
         if (g0 == 0 && glen == n) {
             victims[seg * vstride + pos] = (int32_t)id;
@@ -247,7 +262,7 @@ __global__ __launch_bounds__(TPB) void rank_count_merge_kernel(const uint32_t* _
 // Rows over 32768 keys: merge sorted runs [base, base+run) and [base+run,
 // base+2run) of every segment.  An element counts the other run's keys before
 // it by binary search: keys below it, and for the first run (lower indexes)
-// also keys equal to it.  With klim < n only each run's first klim places take
+// also keys equal to it (padding of the second run counts the whole first run).  With klim < n only each run's first klim places take
 // part (the same argument as for the counting merge).
 __global__ __launch_bounds__(256) void rank_merge_kernel(const uint32_t* __restrict__ in_keys,
                                                          const uint32_t* __restrict__ in_idx,
@@ -275,6 +290,7 @@ __global__ __launch_bounds__(256) void rank_merge_kernel(const uint32_t* __restr
     if (mine >= klim) return;
     if (hi - lo > klim) hi = lo + klim;
     const int64_t first = lo;
+    if (x == kPadKey && pos >= a_end) lo = hi;   // padding of the second run: all of the first comes before
     while (lo < hi) {
         const int64_t mid = lo + ((hi - lo) >> 1);
         if (row[mid] < xr) lo = mid + 1;
@@ -314,8 +330,8 @@ size_t rank_workspace_bytes(int64_t n, int64_t n_seg) {
     return (size_t)((n <= kMaxLdsItems ? 1 : 2) * n * n_seg) * sizeof(uint64_t);
 }
 
-hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int64_t k, int32_t* victims, void* ws,
-                       hipStream_t st) {
+hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int64_t k, RowOrder ro, int32_t* victims,
+                       void* ws, hipStream_t st) {
     if (n <= 0 || n_seg <= 0) return hipSuccess;
     // largest grids of the path this row length takes: the step-1 sort, the
     // second merge level (8 workgroups per run of 8192) and the pairwise merges
@@ -324,15 +340,15 @@ hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int64_t k,
         !grid_fits((n * n_seg + 255) / 256))
         return hipErrorInvalidConfiguration;
     if (n <= 256) {
-        rank_bitonic_kernel<256><<<(unsigned)n_seg, 64, 0, st>>>(scores, n, n, 1, k, k, victims, nullptr, nullptr);
+        rank_bitonic_kernel<256><<<(unsigned)n_seg, 64, 0, st>>>(scores, n, n, 1, k, k, ro, victims, nullptr, nullptr);
         return hipGetLastError();
     }
     if (n <= 1024) {
-        rank_bitonic_kernel<1024><<<(unsigned)n_seg, 256, 0, st>>>(scores, n, n, 1, k, k, victims, nullptr, nullptr);
+        rank_bitonic_kernel<1024><<<(unsigned)n_seg, 256, 0, st>>>(scores, n, n, 1, k, k, ro, victims, nullptr, nullptr);
         return hipGetLastError();
     }
     if (n <= kSingle) {
-        rank_bitonic_kernel<2048><<<(unsigned)n_seg, 512, 0, st>>>(scores, n, n, 1, k, k, victims, nullptr, nullptr);
+        rank_bitonic_kernel<2048><<<(unsigned)n_seg, 512, 0, st>>>(scores, n, n, 1, k, k, ro, victims, nullptr, nullptr);
         return hipGetLastError();
     }
     // workspace: buffer A = run keys then run indexes (4 + 4 bytes per key), and
@@ -344,7 +360,7 @@ hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int64_t k,
     uint32_t* bi = bk + total;
     const int nruns = (int)((n + kChunk - 1) / kChunk);
     rank_bitonic_kernel<kChunk><<<(unsigned)(n_seg * nruns), kChunk / 4, 0, st>>>(scores, n, kChunk, nruns, k, k,
-                                                                                nullptr, ak, ai);
+                                                                                ro, nullptr, ak, ai);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // runs of 1024 -> groups of 8192 (the whole row when it is no longer)

@@ -32,9 +32,6 @@ namespace pred {
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
 constexpr int kWaves = 4;
 #ifndef PRED_PREFILL_CHUNK
 #define PRED_PREFILL_CHUNK 64
@@ -49,19 +46,6 @@ struct PrefillGeom {
     int64_t n_keys;       // n * B keys per sequence
     int64_t groups;       // key groups per (layer, sequence, kv head)
 };
-
-template <int M>
-__device__ inline float lane_xor(float v) {
-    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
-    if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
-    if constexpr (M == 7) return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
-    if constexpr (M == 15) return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true));
-    return __shfl_xor(v, M);
-}
-
-__device__ inline bf16x8_t load8(const uint16_t* p) {
-    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
-}
 
 // R: projected width; NKT: 32-key tiles per wave; BS: block size in tokens.
 template <int R, int NKT, int BS>
@@ -121,7 +105,7 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, Prefill
 
     // query chunk c -> registers (16-byte piece p: query row p / CPR, piece p % CPR)
     const uint16_t* qrows = a.qp + ((int64_t)l * a.S + s) * (int64_t)a.M * a.Hq * R;
-    uint4 gq[PPT];
+    u32x4_t gq[PPT];
     auto load_chunk = [&](int c) {
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
@@ -131,7 +115,7 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, Prefill
                 if (e >= gm.n_eff) e = gm.n_eff - 1;   // padding rows repeat a real query
                 const int row = e / g;
                 const int h = e - row * g;
-                gq[i] = *reinterpret_cast<const uint4*>(qrows + ((int64_t)row * a.Hq + kv * g + h) * R + (p % CPR) * 8);
+                gq[i] = *reinterpret_cast<const u32x4_t*>(qrows + ((int64_t)row * a.Hq + kv * g + h) * R + (p % CPR) * 8);
             }
         }
     };
@@ -140,7 +124,7 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, Prefill
         for (int i = 0; i < PPT; ++i) {
             const int p = tid + 256 * i;
             if (PIECES % 256 == 0 || p < PIECES)
-                *reinterpret_cast<uint4*>(&lds[buf][(p / CPR) * ROWB + (p % CPR) * 16]) = gq[i];
+                *reinterpret_cast<u32x4_t*>(&lds[buf][(p / CPR) * ROWB + (p % CPR) * 16]) = gq[i];
         }
     };
     // one 32-query tile of the chunk in LDS buffer buf

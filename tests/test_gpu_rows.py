@@ -1,0 +1,202 @@
+"""GPU parity of the per-row causal scorer and the per-row keep sets (through the C ABI).
+
+* pred_score_rows against oracle.score_rows, recomputed from the GPU's own A_g,
+  within the score tolerance; -inf exactly where a block is not complete.
+* pred_select_keep bit-exact against oracle.keep_sets of the same float32 scores
+  (the GPU's own scores where they come from pred_score_rows); against the
+  oracle's float64 scores the kept sets agree wherever the k-th and (k+1)-th
+  oracle scores are further apart than the tolerance.
+"""
+
+import numpy as np
+import pytest
+
+import rank_kv_block_amd as rk
+from oracle import bf16, predictor
+from tests.devmem import a_g_layer
+from tests.parity import assert_scores, score_tol
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).cuda()
+
+
+def _randn_bits(rng, shape, scale=1.0):
+    return bf16.encode(rng.standard_normal(shape) * scale)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rk.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _workspace(stride, rows):
+    b = rk.pred_rank_workspace_bytes(stride, rows)
+    return torch.empty((b // 8 + 1,), dtype=torch.int64, device="cuda") if b else None
+
+
+def _check_keep_sets(keep, gpu_scores, oracle_scores, first_pos, ratio, topk, r, what):
+    """(i) exact against the oracle's keep sets of the GPU's scores; (ii) the same sets as the
+    oracle's own float64 order wherever the cut at topk is well separated."""
+    want = predictor.keep_sets(gpu_scores, first_pos, ratio, topk)
+    if not np.array_equal(keep, want):
+        row, col = np.argwhere(keep != want)[0]
+        raise AssertionError(f"{what} (i): row {row} differs first at slot {col}: gpu {keep[row, col]}, "
+                             f"oracle {want[row, col]}")
+    if oracle_scores is None:
+        return
+    for i in range(keep.shape[0]):
+        c = predictor.complete_blocks(first_pos, i, ratio, oracle_scores.shape[1])
+        if c <= topk:
+            assert set(keep[i, :c].tolist()) == set(range(c)), (what, i)
+            continue
+        o = oracle_scores[i, :c]
+        srt = np.sort(o)[::-1]
+        gap = srt[topk - 1] - srt[topk]
+        if gap > 2 * score_tol(np.array([srt[topk - 1]]), r)[0]:
+            assert set(keep[i].tolist()) == set(np.argsort(-o, kind="stable")[:topk].tolist()), (what, i)
+
+
+# ------------------------------------------------------------- per-row scores
+
+ROW_SHAPES = [
+    # Hq, Hk, D, R, B, N, n, rows, first_pos, stride, table         path
+    (32, 8, 64, 32, 16, 40, 40, 70, 500, 40, "perm"),             # mfma, every block complete late on
+    (32, 8, 64, 32, 16, 40, 37, 45, 0, 43, "perm"),               # mfma, causal from position 0, tail columns
+    (8, 2, 64, 64, 8, 96, 90, 100, 640, 90, "identity"),          # mfma, NKT 4 with R 64 / Hk 2
+    (4, 4, 32, 16, 32, 20, 20, 33, 37, 25, "identity"),           # mfma, B 32, g 1
+    (8, 1, 64, 128, 16, 24, 24, 64, 200, 24, "perm"),             # mfma, R 128
+    (6, 1, 64, 16, 8, 30, 30, 31, 100, 28, "perm"),               # mfma, Hq not a multiple of 4, stride < n
+    (64, 8, 64, 64, 32, 12, 12, 40, 300, 12, "identity"),         # mfma, g 8 (two stages per kv head)
+    (6, 3, 32, 16, 16, 20, 20, 40, 100, 22, "perm"),              # plain kernel (Hk 3)
+    (4, 2, 32, 24, 16, 20, 20, 40, 250, 20, "identity"),          # plain kernel (R 24)
+]
+
+
+@pytest.mark.parametrize("shape", ROW_SHAPES)
+def test_score_rows_parity(shape):
+    Hq, Hk, D, R, B, N, n, rows, first_pos, stride, table = shape
+    _say("score_rows", shape)
+    rng = np.random.default_rng(sum((i + 1) * v for i, v in enumerate(shape[:-1])))
+    d = rk.dims(2, Hq, Hk, D, R, B, N)
+    with rk.Predictor(d, 77 + R) as p:
+        phys = rng.permutation(N)[:n].astype(np.int32) if table == "perm" else np.arange(n, dtype=np.int32)
+        k = _randn_bits(rng, (1, n, B, Hk, D))
+        rk.pred_project_kv_block(p.handle, 1, _to_dev(k).view(torch.bfloat16),
+                                 torch.from_numpy(phys.reshape(1, n)).cuda())
+        q = _randn_bits(rng, (rows, Hq, R))
+        sc = torch.full((rows, stride), 12345.0, dtype=torch.float32, device="cuda")
+        tab = None if table == "identity" else torch.from_numpy(phys).cuda()
+        rk.pred_score_rows(p.handle, 1, _to_dev(q).view(torch.bfloat16), first_pos, tab, n, sc)
+        got = sc.cpu().numpy()
+        rk.pred_device_error(p.handle)
+        slots = a_g_layer(p.handle, d, 1)[phys]
+        want = predictor.score_rows(q, slots, first_pos, stride)
+        masked = np.isneginf(want)
+        assert np.array_equal(np.isneginf(got), masked), "-inf exactly where a block is not complete"
+        assert_scores(got[~masked], want[~masked], R, "score_rows")
+        # and the keep sets built on them
+        for topk in (1, 5, min(stride, 16)):
+            keep = torch.full((rows, topk), -7, dtype=torch.int32, device="cuda")
+            rk.pred_select_keep(p.handle, sc, first_pos, B, topk, keep, _workspace(stride, rows))
+            _check_keep_sets(keep.cpu().numpy(), got, want, first_pos, B, topk, R, f"keep {shape} k={topk}")
+
+
+def test_score_rows_edge_cases():
+    """No blocks, no complete block for any row, one row, and an invalid table entry (NaN + error)."""
+    d = rk.dims(1, 8, 2, 32, 32, 16, 16)
+    rng = np.random.default_rng(4)
+    with rk.Predictor(d, 5, flags=rk.PRED_FLAG_ZERO_AG) as p:
+        q = _to_dev(_randn_bits(rng, (40, 8, 32))).view(torch.bfloat16)
+        _say("score_rows n=0")
+        sc = torch.zeros((40, 9), dtype=torch.float32, device="cuda")
+        rk.pred_score_rows(p.handle, 0, q, 10, None, 0, sc)
+        assert np.isneginf(sc.cpu().numpy()).all()
+        _say("score_rows nothing complete")
+        sc = torch.zeros((40, 16), dtype=torch.float32, device="cuda")
+        rk.pred_score_rows(p.handle, 0, q[:10], 0, None, 16, sc[:10])   # positions 0..9 < block_size
+        assert np.isneginf(sc[:10].cpu().numpy()).all()
+        _say("score_rows one row")
+        sc1 = torch.zeros((1, 16), dtype=torch.float32, device="cuda")
+        rk.pred_score_rows(p.handle, 0, q[:1], 16 * 5 - 1, None, 16, sc1)
+        got = sc1.cpu().numpy()
+        assert np.isfinite(got[0, :5]).all() and np.isneginf(got[0, 5:]).all()
+        assert np.all(got[0, :5] == 0.0)   # A_g zeroed
+        _say("score_rows invalid table entry")
+        tab = torch.tensor([0, 1, 99, 3], dtype=torch.int32, device="cuda")
+        sc = torch.zeros((4, 4), dtype=torch.float32, device="cuda")
+        rk.pred_score_rows(p.handle, 0, q[:4], 100, tab, 4, sc)
+        got = sc.cpu().numpy()
+        assert np.isnan(got[:, 2]).all() and np.isfinite(got[:, [0, 1, 3]]).all()
+        with pytest.raises(rk.PredError) as e:
+            rk.pred_device_error(p.handle)
+        assert e.value.code == rk.PRED_ERR_DEVICE
+        with pytest.raises(rk.PredError) as e:
+            rk.pred_score_rows(p.handle, 1, q[:4], 0, None, 4, sc)   # layer 1 of 1
+        assert e.value.code == rk.PRED_ERR_OUT_OF_RANGE
+
+
+# ------------------------------------------------------------- keep sets alone
+
+KEEP_SHAPES = [
+    # rows, stride, first_pos, ratio, topks                        path
+    (9, 7, 0, 1, (0, 1, 3, 7)),                                    # one workgroup (256)
+    (33, 300, 0, 2, (1, 64, 300)),                                 # one workgroup (1024); rows without blocks
+    (16, 2048, 30000, 16, (1, 64, 2048)),                          # one workgroup (2048)
+    (5, 2049, 1500, 1, (1, 64, 2049)),                             # chunked, one merge level
+    (4, 5000, 1 << 20, 1, (1, 64, 5000)),                          # chunked, every block complete
+    (7, 9000, 4000, 1, (1, 100, 9000)),                            # two merge levels
+    (3, 40000, 39990, 1, (1, 1000, 40000)),                        # pairwise merges
+]
+
+
+@pytest.mark.parametrize("rows,stride,first_pos,ratio,topks", KEEP_SHAPES)
+def test_select_keep_exact(rows, stride, first_pos, ratio, topks):
+    rng = np.random.default_rng(rows * 7 + stride)
+    s = (rng.integers(-300, 300, size=(rows, stride)) * 0.25).astype(np.float32)   # many ties
+    s[:, ::41] = -0.0
+    s[:, 3::97] = np.nan
+    s[:, 5::89] = np.inf
+    s[-1, :] = 1.0                                                                  # one row all equal
+    d = rk.dims(1, 1, 1, 8, 8, 1, 1)
+    with rk.Predictor(d, 1) as p:
+        sc = torch.from_numpy(s).cuda()
+        ws = _workspace(stride, rows)
+        for topk in topks:
+            _say("select_keep", rows, stride, first_pos, ratio, topk)
+            keep = torch.full((rows, topk), -7, dtype=torch.int32, device="cuda")
+            rk.pred_select_keep(p.handle, sc, first_pos, ratio, topk, keep, ws)
+            got = keep.cpu().numpy()
+            want = predictor.keep_sets(s, first_pos, ratio, topk)
+            assert np.array_equal(got, want), (rows, stride, topk)
+
+
+def test_select_keep_errors():
+    d = rk.dims(1, 1, 1, 8, 8, 1, 1)
+    with rk.Predictor(d, 1) as p:
+        sc = torch.zeros((4, 3000), dtype=torch.float32, device="cuda")
+        keep = torch.empty((4, 8), dtype=torch.int32, device="cuda")
+        with pytest.raises(rk.PredError) as e:
+            rk.pred_select_keep(p.handle, sc, 0, 1, 8, keep, None)
+        assert e.value.code == rk.PRED_ERR_WORKSPACE
+        ws = _workspace(3000, 4)
+        for first_pos, ratio in ((0, 0), (-1, 4)):
+            with pytest.raises(rk.PredError) as e:
+                rk.pred_select_keep(p.handle, sc, first_pos, ratio, 8, keep, ws)
+            assert e.value.code == rk.PRED_ERR_OUT_OF_RANGE
+        with pytest.raises(rk.PredError) as e:
+            rk.pred_select_keep(p.handle, sc, 0, 1, 3001, torch.empty((4, 3001), dtype=torch.int32, device="cuda"), ws)
+        assert e.value.code == rk.PRED_ERR_OUT_OF_RANGE
+        rk.pred_select_keep(p.handle, sc, 0, 1, 0, torch.empty((4, 0), dtype=torch.int32, device="cuda"), ws)

@@ -328,3 +328,96 @@ def test_select_is_the_sorted_prefix():
                 vals = [float(v) for v in s[row]]
                 want = sorted(range(n), key=lambda b: (_key_py(vals[b]), b))[:k]
                 assert got[row].tolist() == want
+
+
+# ------------------------------------------------- per-row causal keep sets
+
+def _f(x):
+    return np.array([[float(v) for v in row] for row in x])
+
+
+def test_hand_keep(golden_dir):
+    g = _load(golden_dir, "hand_keep.json")
+    rc = g["rows_case"]
+    s = predictor.score_rows(_bits(rc["q_proj"]), _bits(rc["slots"]), rc["first_pos"], rc["stride"])
+    assert np.array_equal(s, _f(rc["scores"]))
+    keep = predictor.keep_sets(s.astype(np.float32), rc["first_pos"], 2, 2)
+    assert keep.tolist() == rc["keep_top2"]
+    kc = g["keep_case"]
+    s = _f(kc["scores"]).astype(np.float32)
+    assert predictor.keep_sets(s, kc["first_pos"], kc["ratio"], 2).tolist() == kc["keep_top2"]
+    assert predictor.keep_sets(s, kc["first_pos"], kc["ratio"], 3).tolist() == kc["keep_top3"]
+
+
+def _keep_py(row, c, topk):
+    """The page's comparator written out: larger score first, then lower index; NaN after numbers."""
+    import functools
+
+    def cmp(a, b):
+        va, vb = float(row[a]), float(row[b])
+        na, nb = va != va, vb != vb
+        if na != nb:
+            return 1 if na else -1
+        if not na and va != vb:
+            return -1 if va > vb else 1
+        return -1 if a < b else (1 if a > b else 0)
+
+    order = sorted(range(c), key=functools.cmp_to_key(cmp))[:topk]
+    return order + [-1] * (topk - len(order))
+
+
+def test_keep_sets_match_python_sorted():
+    rng = np.random.default_rng(77)
+    for trial in range(60):
+        rows = int(rng.integers(1, 7))
+        stride = int(rng.integers(1, 40))
+        ratio = int(rng.integers(1, 9))
+        first_pos = int(rng.integers(0, 3 * stride))
+        topk = int(rng.integers(0, stride + 1))
+        s = (rng.integers(-6, 6, size=(rows, stride)) * 0.5).astype(np.float32)   # many ties
+        s[rng.random(s.shape) < 0.1] = -0.0
+        s[rng.random(s.shape) < 0.05] = np.nan
+        s[rng.random(s.shape) < 0.05] = -np.inf
+        got = predictor.keep_sets(s, first_pos, ratio, topk)
+        for i in range(rows):
+            # complete blocks: every one of the block's ratio positions is at or before the row's
+            c = sum(1 for b in range(stride) if (b + 1) * ratio - 1 <= first_pos + i)
+            assert got[i].tolist() == _keep_py(s[i], c, topk), (trial, i)
+
+
+def test_keep_sets_are_prefixes():
+    rng = np.random.default_rng(5)
+    s = rng.standard_normal((9, 50)).astype(np.float32)
+    full = predictor.keep_sets(s, 40, 4, 50)
+    for k in (0, 1, 7, 11, 50):
+        assert np.array_equal(predictor.keep_sets(s, 40, 4, k), full[:, :k])
+
+
+def test_score_rows_brute_force():
+    rng = np.random.default_rng(12)
+    rows, Hq, Hk, R, B, n = 5, 4, 2, 3, 3, 4
+    q = _rand_bits(rng, (rows, Hq, R))
+    a = _rand_bits(rng, (n, Hk, B, R))
+    qd, ad = bf16.decode(q), bf16.decode(a)
+    for first_pos in (0, 2, 6, 30):
+        for stride in (3, 4, 6):
+            got = predictor.score_rows(q, a, first_pos, stride)
+            for i in range(rows):
+                for b in range(stride):
+                    visible = b < n and (b + 1) * B - 1 <= first_pos + i
+                    if not visible:
+                        assert got[i, b] == -np.inf
+                        continue
+                    best = max(sum(float(qd[i, h, j]) * float(ad[b, h // (Hq // Hk), t, j]) for j in range(R))
+                               for h in range(Hq) for t in range(B))
+                    assert abs(got[i, b] - best) <= 1e-12 * max(1.0, abs(best)), (first_pos, stride, i, b)
+
+
+def test_score_rows_all_complete_reduces_to_score_blocks():
+    """When every block is complete for every row, the max over rows is score_blocks' score."""
+    rng = np.random.default_rng(3)
+    q = _rand_bits(rng, (6, 8, 16))
+    a = _rand_bits(rng, (10, 2, 4, 16))
+    s = predictor.score_rows(q, a, 10 * 4, 10)
+    assert np.isfinite(s).all()
+    assert np.allclose(s.max(axis=0), predictor.score_one(q, a), rtol=1e-12, atol=1e-12)
