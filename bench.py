@@ -162,8 +162,10 @@ def main():
 
     # per-call breakdown of a step, in a separate loop so the timed steps above
     # carry no extra events: median of 20 steps per entry point
-    names = ["project_kv_block", "project_q", "score_blocks", "rank_victims"]
+    names = ["project_kv_block", "project_q", "score_blocks", "rank_victims", "score_blocks_masked"]
     evs = {k: [] for k in names}
+    # the decode case of a partly filled last block: half of block_size + 1 tokens in every sequence
+    fill = torch.full((c.S,), c.B // 2 + 1, dtype=torch.int32, device="cuda")
     for i in range(20):
         l0 = wl.layer0_for_step(i)
         calls = [
@@ -171,6 +173,7 @@ def main():
             lambda: rk.pred_project_q(wl.h, wl.q[l0:l0 + nl], wl.q_proj),
             lambda: rk.pred_score_blocks(wl.h, l0, wl.q_proj, wl.tables, wl.scores),
             lambda: rk.pred_rank_victims(wl.h, wl.scores.view(nl * c.S, c.n), wl.victims, wl.workspace),
+            lambda: rk.pred_score_blocks_masked(wl.h, l0, wl.q_proj, wl.tables, fill, wl.scores),
         ]
         for name, call in zip(names, calls):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -196,6 +199,41 @@ def main():
     torch.cuda.synchronize()
     tk = sorted(a.elapsed_time(b) for a, b in evk)
     breakdown[f"select_victims_k{k_sel}"] = round(tk[len(tk) // 2] * 1e3, 2)
+
+    # per-row causal scores and keep sets of the first layer and sequence (many-row
+    # workloads): each query row against the blocks complete at its position, then
+    # every row's top-k; timed per entry point, median of 20
+    keep_sets = None
+    if c.M > 1:
+        wl.keep_setup(64)
+        evr, evs_k = [], []
+        for i in range(20):
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            tab = None if wl.tables is None else wl.tables[0]
+            e0.record(stream)
+            rk.pred_score_rows(wl.h, 0, wl.q_proj[0, 0], c.first_pos, tab, c.n, wl.row_scores)
+            e1.record(stream)
+            rk.pred_select_keep(wl.h, wl.row_scores, c.first_pos, c.B, wl.topk, wl.keep, wl.keep_ws)
+            e2.record(stream)
+            evr.append((e0, e1))
+            evs_k.append((e1, e2))
+        torch.cuda.synchronize()
+        rk.pred_device_error(wl.h)
+        tr = sorted(a.elapsed_time(b) for a, b in evr)
+        ts = sorted(a.elapsed_time(b) for a, b in evs_k)
+        # algorithmic work: every complete (row, block) pair, all heads and tokens
+        pairs = sum(c.complete_blocks(i) for i in range(c.M))
+        rflops = 2.0 * pairs * c.B * c.Hq * c.R
+        r_med = tr[len(tr) // 2]
+        r_ach = rflops / (r_med * 1e-3) / 1e12
+        keep_sets = {"rows": c.M, "blocks": c.n, "first_pos": c.first_pos, "topk": wl.topk,
+                     "score_rows_us": {"median": round(r_med * 1e3, 2), "min": round(tr[0] * 1e3, 2),
+                                       "max": round(tr[-1] * 1e3, 2)},
+                     "select_keep_us": {"median": round(ts[len(ts) // 2] * 1e3, 2), "min": round(ts[0] * 1e3, 2),
+                                        "max": round(ts[-1] * 1e3, 2)},
+                     "roofline": {"bound": "mfma", "achieved": round(r_ach, 2), "peak": MFMA_BF16_PEAK_TFS,
+                                  "unit": "TFLOP/s", "frac": round(r_ach / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                                  "kernel": "score_rows_kernel", "algorithmic_flops_per_launch": rflops}}
 
     # the same layers scored one per call (a per-layer decode loop), each layer in turn
     per_layer = None
@@ -261,6 +299,8 @@ def main():
     out["step_breakdown_median_us"] = breakdown
     if per_layer is not None:
         out["score_per_layer_call"] = per_layer
+    if keep_sets is not None:
+        out["keep_sets"] = keep_sets
     if not args.no_cpu_baseline:
         print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)

@@ -147,6 +147,17 @@ int pred_score_blocks(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf
                       int32_t n_rows, const int32_t* block_tables, int64_t n_blocks, int32_t n_seqs,
                       float* scores, void* stream);
 
+/* As pred_score_blocks, but the last block of each sequence (logical block
+ * n_blocks - 1) is partly filled: only its first last_fill[s] tokens are scored
+ * (a decode step appends one token at a time; the predictor.rs page scores all
+ * block_size tokens of every block, which equals last_fill[s] = block_size).
+ *   last_fill  device, [n_seqs] int32 in [0, block_size], or NULL for full blocks.
+ * A last block with fill 0 scores -inf.  A value outside [0, block_size] is
+ * clamped to it and raises the device error word (see pred_device_error). */
+int pred_score_blocks_masked(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* q_proj,
+                             int32_t n_rows, const int32_t* block_tables, int64_t n_blocks, int32_t n_seqs,
+                             const int32_t* last_fill, float* scores, void* stream);
+
 /* Eviction order (predictor.rs page, module doc: scores rank eviction victims;
  * qsa_select.rs page, host top-k: lower index on ties).
  *   scores     device, [n_segments, n_blocks] float32
@@ -243,7 +254,8 @@ int pred_read_slot(pred_t* p, int32_t layer, int64_t block, pred_bf16* host_out,
 int pred_get_dims(pred_t* p, pred_dims* out);
 
 /* Synchronise `stream`, read and clear the device error word.  Returns 0, or
- * PRED_ERR_DEVICE if a kernel since the last call met an invalid table entry. */
+ * PRED_ERR_DEVICE if a kernel since the last call met an invalid table entry
+ * or a last-block fill count outside [0, block_size]. */
 int pred_device_error(pred_t* p, void* stream);
 
 /* Message for the last failing call on this thread ("" if none). */

@@ -20,7 +20,9 @@ Readings where the pages leave a step open:
 * scores and ranks are indexed by a block's *logical* position in its sequence's
   block table (an absent table is the identity, which is the pages' contiguous
   ``k_lr_seq`` case); ties rank the lower logical index first;
-* every one of a block's B tokens is scored (no fill length is passed);
+* every one of a block's B tokens is scored (the pages pass no fill length);
+  the masked variant scores only the first ``last_fill[s]`` tokens of a
+  sequence's last block (fill 0: -inf);
 * ranking key: -0 is +0, every NaN ranks first;
 * per-row keep sets (the qsa_select.rs page's prefill selection, rebuilt on the
   predictor's score): a row at position p sees blocks ``b < (p + 1) // B`` (the
@@ -84,13 +86,20 @@ def project_kv_block(a_g, layer, k_bits, table, p_bits):
 
 # ---------------------------------------------------------------------- scores
 
-def score_one(q_rows, slots):
+def score_one(q_rows, slots, last_fill=None):
     """Scores of one (layer, sequence) in float64.
 
     ``q_rows [M, Hq, R]`` bf16 projected queries; ``slots [n, Hk, B, R]`` bf16
     low-rank keys of the sequence's blocks in logical order.  Returns ``[n]``:
     ``max over i < M, h < Hq, t < B of sum_j q[i, h, j] * A[b, h // g, t, j]``.
+    With ``last_fill`` the last block (b = n - 1) holds only its first
+    ``last_fill`` tokens and the max runs over those (-inf when there are none).
     """
+    if last_fill is not None and len(slots):
+        out = score_one(q_rows, slots)
+        f = max(0, min(int(last_fill), slots.shape[2]))
+        out[-1] = score_one(q_rows, slots[-1:, :, :f])[0] if f else -np.inf
+        return out
     q = bf16.decode(q_rows)
     M, Hq, R = q.shape
     n, Hk, B, _ = slots.shape
@@ -110,19 +119,21 @@ def score_one(q_rows, slots):
     return out
 
 
-def score_blocks(q_proj, a_g, layer0, tables, n_blocks):
+def score_blocks(q_proj, a_g, layer0, tables, n_blocks, last_fill=None):
     """``score_blocks`` for ``n_layers`` layers and ``S`` sequences, float64.
 
     ``q_proj [n_layers, S, M, Hq, R]`` bf16; ``a_g [L, N, Hk, B, R]`` bf16;
     ``tables [S, n_blocks]`` int physical ids, or None for the identity (the
-    pages' contiguous slots ``0..n-1``).  Returns ``[n_layers, S, n_blocks]``.
+    pages' contiguous slots ``0..n-1``); ``last_fill [S]`` tokens held by each
+    sequence's last block, or None for full blocks.  Returns ``[n_layers, S, n_blocks]``.
     """
     n_layers, S = q_proj.shape[0], q_proj.shape[1]
     out = np.empty((n_layers, S, n_blocks))
     for l in range(n_layers):
         for s in range(S):
             ids = np.arange(n_blocks) if tables is None else np.asarray(tables[s])[:n_blocks]
-            out[l, s] = score_one(q_proj[l, s], a_g[layer0 + l][ids])
+            fill = None if last_fill is None else last_fill[s]
+            out[l, s] = score_one(q_proj[l, s], a_g[layer0 + l][ids], fill)
     return out
 
 

@@ -167,6 +167,26 @@ def pred_score_blocks(h, layer0, q_proj, block_tables, scores, stream=None):
                                    _ptr(scores, "scores", (torch.float32,)), _stream(stream)))
 
 
+def pred_score_blocks_masked(h, layer0, q_proj, block_tables, last_fill, scores, stream=None):
+    """As pred_score_blocks; last_fill [n_seqs] int32 (or None) = tokens held by each sequence's last block."""
+    import torch
+    d = pred_get_dims(h)
+    if q_proj.dim() != 5 or tuple(q_proj.shape[3:]) != (d.num_q_heads, d.r):
+        raise ValueError(f"q_proj must be [n_layers, n_seqs, n_rows, {d.num_q_heads}, {d.r}]")
+    n_layers, n_seqs, n_rows = q_proj.shape[:3]
+    if scores.dim() != 3 or tuple(scores.shape[:2]) != (n_layers, n_seqs):
+        raise ValueError("scores must be [n_layers, n_seqs, n_blocks]")
+    n_blocks = scores.shape[2]
+    if block_tables is not None and tuple(block_tables.shape) != (n_seqs, n_blocks):
+        raise ValueError("block_tables must be [n_seqs, n_blocks]")
+    if last_fill is not None and tuple(last_fill.shape) != (n_seqs,):
+        raise ValueError("last_fill must be [n_seqs]")
+    _check(lib().pred_score_blocks_masked(h, layer0, n_layers, _ptr(q_proj, "q_proj", _bf16_types()), n_rows,
+                                          _ptr(block_tables, "block_tables", (torch.int32,)), n_blocks, n_seqs,
+                                          _ptr(last_fill, "last_fill", (torch.int32,)),
+                                          _ptr(scores, "scores", (torch.float32,)), _stream(stream)))
+
+
 def pred_rank_victims(h, scores, victims, workspace=None, stream=None):
     """scores [n_segments, n_blocks] float32 -> victims [n_segments, n_blocks] int32."""
     import torch

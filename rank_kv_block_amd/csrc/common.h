@@ -8,7 +8,7 @@
 namespace pred {
 
 // Bits of the device error word.
-enum : uint32_t { DEVERR_TABLE = 1u };
+enum : uint32_t { DEVERR_TABLE = 1u, DEVERR_FILL = 2u };
 
 __host__ __device__ inline uint64_t f64_bits(double x) {
 #if defined(__HIP_DEVICE_COMPILE__)

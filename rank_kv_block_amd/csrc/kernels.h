@@ -27,12 +27,20 @@ struct ScoreArgs {
     const uint16_t* qp;     // [n_layers, S, M, Hq, R]
     const uint16_t* ag;     // A_g base [L, N, Hk, B, R]
     const int32_t* tables;  // [S, n] or null
+    const int32_t* fill;    // [S] tokens held by each sequence's last block (n - 1), or null (all B)
     float* scores;          // [n_layers, S, n]
     uint32_t* err;
     int64_t N;              // max_blocks
     int64_t n;              // blocks per sequence
     int layer0, n_layers, S, M, Hq, Hk, B, R;
 };
+// Tokens of block b of sequence s that are scored: B, except the last block
+// with a fill array (clamped to [0, B]; a value outside raises DEVERR_FILL).
+__device__ inline int fill_of(const ScoreArgs& a, int s) {
+    if (!a.fill) return a.B;
+    const int f = a.fill[s];
+    return f < 0 ? 0 : (f > a.B ? a.B : f);
+}
 // Streaming decode scorer when the shape allows it, else a plain per-block kernel.
 hipError_t launch_score_decode_or_generic(const ScoreArgs& a, hipStream_t stream);
 const char* score_decode_path_name(const ScoreArgs& a);

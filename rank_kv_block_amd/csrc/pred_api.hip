@@ -250,8 +250,11 @@ int pred_project_kv_block(pred_t* p, int32_t layer0, int32_t n_layers, const pre
     return ok();
 }
 
-int pred_score_blocks(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* q_proj, int32_t n_rows,
-                      const int32_t* block_tables, int64_t n_blocks, int32_t n_seqs, float* scores, void* stream) {
+namespace {
+
+int score_impl(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* q_proj, int32_t n_rows,
+               const int32_t* block_tables, int64_t n_blocks, int32_t n_seqs, const int32_t* last_fill,
+               float* scores, void* stream) {
     if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
     if (layer0 < 0 || n_layers < 0 || (int64_t)layer0 + n_layers > p->d.num_layers)
         return fail(PRED_ERR_OUT_OF_RANGE, "score_blocks layers [%d, %d) outside [0, %d)", layer0, layer0 + n_layers,
@@ -270,6 +273,7 @@ int pred_score_blocks(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf
     a.qp = q_proj;
     a.ag = p->ag_dev;
     a.tables = block_tables;
+    a.fill = last_fill;
     a.scores = scores;
     a.err = p->err_dev;
     a.N = p->d.max_blocks;
@@ -288,6 +292,20 @@ int pred_score_blocks(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf
     else e = pred::launch_score_decode_or_generic(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "score_blocks launch");
     return ok();
+}
+
+}  // namespace
+
+int pred_score_blocks(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* q_proj, int32_t n_rows,
+                      const int32_t* block_tables, int64_t n_blocks, int32_t n_seqs, float* scores, void* stream) {
+    return score_impl(p, layer0, n_layers, q_proj, n_rows, block_tables, n_blocks, n_seqs, nullptr, scores, stream);
+}
+
+int pred_score_blocks_masked(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* q_proj, int32_t n_rows,
+                             const int32_t* block_tables, int64_t n_blocks, int32_t n_seqs, const int32_t* last_fill,
+                             float* scores, void* stream) {
+    return score_impl(p, layer0, n_layers, q_proj, n_rows, block_tables, n_blocks, n_seqs, last_fill, scores,
+                      stream);
 }
 
 int pred_score_rows(pred_t* p, int32_t layer, const pred_bf16* q_proj, int64_t rows, int64_t first_pos,
@@ -430,7 +448,9 @@ int pred_device_error(pred_t* p, void* stream) {
     if (w) {
         e = hipMemset(p->err_dev, 0, 4);
         if (e != hipSuccess) return hip_fail(e, "clear error word");
-        return fail(PRED_ERR_DEVICE, "a kernel met a block-table entry outside [0, max_blocks) (flags 0x%x)", w);
+        return fail(PRED_ERR_DEVICE, "%s%s(flags 0x%x)",
+                    (w & 1u) ? "a kernel met a block-table entry outside [0, max_blocks) " : "",
+                    (w & 2u) ? "a last-block fill count was outside [0, block_size] " : "", w);
     }
     return ok();
 }

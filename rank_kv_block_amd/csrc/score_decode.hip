@@ -160,6 +160,10 @@ void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
         const int64_t b = b_first + lane;
         if (lane < gm.NBW && b < a.n) tab_lane = a.tables ? a.tables[(int64_t)s * a.n + b] : (int32_t)b;
     }
+    // the sequence's last block holds fill_s tokens; its other rows are left out
+    // of the max (only the live bit of their slots changes, nothing per step)
+    const int fill_s = fill_of(a, s);
+    if (a.fill && wgb == 0 && threadIdx.x == 0 && (a.fill[s] < 0 || a.fill[s] > a.B)) atomicOr(a.err, DEVERR_FILL);
     Off voff[NS];
     uint32_t soff_slot[NS];   // UNI: the whole slot offset is wave-uniform (SGPR)
     uint32_t live = 0;
@@ -175,7 +179,8 @@ void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
         voff[sl] = (Off)(((ok ? (int64_t)phys : 0) * slot_elems + (int64_t)t * a.R + p * 8) * 2);
         // UNI: row t, lane part p of slot sl is byte 1024 * (sl % SPB) + 16 * lane of the block's region
         soff_slot[sl] = (uint32_t)((ok ? (int64_t)phys : 0) * slot_elems * 2 + 1024 * (sl % gm.SPB));
-        live |= (ok ? 1u : 0u) << sl;
+        const bool cut = b_first + bi == a.n - 1 && t >= fill_s;
+        live |= ((ok && !cut) ? 1u : 0u) << sl;
     }
 
     float rm[NS];
@@ -343,12 +348,14 @@ __global__ __launch_bounds__(256) void score_generic_kernel(ScoreArgs a) {
     }
     const uint16_t* slot = a.ag + ((a.layer0 + l) * a.N + phys) * (int64_t)a.Hk * a.B * a.R;
     const uint16_t* qrows = a.qp + ((int64_t)l * a.S + s) * (int64_t)a.M * a.Hq * a.R;
+    const int n_tok = b == a.n - 1 ? fill_of(a, s) : a.B;
+    if (a.fill && b == a.n - 1 && l == 0 && (a.fill[s] < 0 || a.fill[s] > a.B)) atomicOr(a.err, DEVERR_FILL);
     float best = -__builtin_inff();
     for (int i = 0; i < a.M; ++i)
         for (int h = 0; h < a.Hq; ++h) {
             const uint16_t* qv = qrows + ((int64_t)i * a.Hq + h) * a.R;
             const uint16_t* kbase = slot + (int64_t)(h / g) * a.B * a.R;
-            for (int t = 0; t < a.B; ++t) {
+            for (int t = 0; t < n_tok; ++t) {
                 float acc = 0.0f;
                 for (int j = 0; j < a.R; ++j)
                     acc = __builtin_fmaf(__uint_as_float((uint32_t)qv[j] << 16),

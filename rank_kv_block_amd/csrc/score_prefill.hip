@@ -169,8 +169,15 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, Prefill
     if (!active) return;
 
     uint32_t* out = keys + ((int64_t)l * a.S + s) * a.n;
+    const int fill_s = fill_of(a, s);   // tokens of the last block that are scored
+    if (a.fill && grp == 0 && kv == 0 && part == 0 && l == 0 && tid == 0 && (a.fill[s] < 0 || a.fill[s] > BS))
+        atomicOr(a.err, DEVERR_FILL);
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
+        {
+            const int64_t key = key0 + t * 32 + col;
+            if (key / BS == a.n - 1 && (int)(key % BS) >= fill_s) rm[t] = -__builtin_inff();
+        }
         float v = fmaxf(rm[t], lane_xor<32>(rm[t]));   // rows split across the two lane halves
         v = fmaxf(v, lane_xor<1>(v));
         v = fmaxf(v, lane_xor<2>(v));

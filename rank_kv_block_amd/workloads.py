@@ -25,7 +25,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (PRED_FLAG_ZERO_AG, dims, pred_create, pred_destroy, pred_project_kv_block,  # noqa: F401
-               pred_project_q, pred_rank_victims, pred_rank_workspace_bytes, pred_score_blocks)
+               pred_project_q, pred_rank_victims, pred_rank_workspace_bytes, pred_score_blocks,
+               pred_score_rows, pred_select_keep)
 from . import synth
 
 
@@ -69,6 +70,15 @@ class Config:
     @property
     def blocks_per_step(self):
         return self.step_layers * self.S * self.n
+
+    @property
+    def first_pos(self):
+        """Position of the first query row: the rows are the context's last M tokens."""
+        return self.n * self.B - self.M
+
+    def complete_blocks(self, row):
+        """Blocks every token of which is at or before query row ``row``'s position."""
+        return min(self.n, (self.first_pos + row + 1) // self.B)
 
 
 CONFIGS = {
@@ -167,6 +177,24 @@ class Workload:
         ws = pred_rank_workspace_bytes(c.n, nl * c.S)
         self.workspace = torch.empty((max(ws, 8) // 8,), dtype=torch.int64, device=device) if ws else None
         torch.cuda.synchronize()
+
+    def keep_setup(self, topk=64):
+        """Buffers for the per-row keep sets of the first scored layer and sequence."""
+        c = self.cfg
+        self.topk = min(topk, c.n)
+        self.row_scores = torch.empty((c.M, c.n), dtype=torch.float32, device=self.device)
+        self.keep = torch.empty((c.M, self.topk), dtype=torch.int32, device=self.device)
+        ws = pred_rank_workspace_bytes(c.n, c.M)
+        self.keep_ws = torch.empty((max(ws, 8) // 8,), dtype=torch.int64, device=self.device) if ws else None
+
+    def keep_step(self, l0=0, stream=None):
+        """Per-row causal scores of the step's first layer and sequence 0 (from q_proj of the
+        last step) and each row's keep set of topk blocks."""
+        c = self.cfg
+        tab = None if self.tables is None else self.tables[0]
+        pred_score_rows(self.h, l0, self.q_proj[0, 0], c.first_pos, tab, c.n, self.row_scores, stream=stream)
+        pred_select_keep(self.h, self.row_scores, c.first_pos, c.B, self.topk, self.keep, self.keep_ws,
+                         stream=stream)
 
     def layer0_for_step(self, i):
         c = self.cfg

@@ -129,3 +129,41 @@ def test_config_long_context_70b():
 
 def test_config_llama3_8b_decode_on_a_second_stream():
     _check_workload("llama3_8b_decode", full_layers=1, sample_blocks=32, keep_per_layer=2, side_stream=True)
+
+
+def test_config_prefill_chunk_keep_sets():
+    """Per-row causal scores and keep sets at the prefill chunk's full size (2048 rows x 2048 blocks,
+    rows at positions 30720..32767), launched as bench.py times them: sampled rows against the
+    oracle, the causal mask and every row's keep set exactly."""
+    from rank_kv_block_amd.workloads import CONFIGS, Workload
+    import rank_kv_block_amd as rk
+    c = CONFIGS["prefill_chunk"]
+    _say("prefill_chunk keep sets: setup")
+    wl = Workload(c)
+    try:
+        wl.keep_setup(64)
+        _say("prefill_chunk keep sets: step")
+        wl.step(0)
+        wl.keep_step(0)
+        torch.cuda.synchronize()
+        rk.pred_device_error(wl.h)
+        got = wl.row_scores.cpu().numpy()
+        keep = wl.keep.cpu().numpy()
+        qp = _bits(wl.q_proj[0, 0])                                   # [M, Hq, R]
+        slots = a_g_layer(wl.h, wl.d, 0)[wl.phys[0].numpy()]         # logical order
+        for i in range(c.M):
+            cnt = c.complete_blocks(i)
+            assert np.isfinite(got[i, :cnt]).all() and np.isneginf(got[i, cnt:]).all(), i
+        rng = np.random.default_rng(44)
+        rows = sorted(set(rng.choice(c.M, 40, replace=False).tolist()) | {0, 15, 16, c.M - 1})
+        _say("prefill_chunk keep sets: oracle rows", len(rows))
+        for i in rows:
+            want = predictor.score_rows(qp[i:i + 1], slots, c.first_pos + i, c.n)[0]
+            m = np.isneginf(want)
+            assert np.array_equal(np.isneginf(got[i]), m), i
+            assert_scores(got[i][~m], want[~m], c.R, f"row scores, row {i}")
+        _say("prefill_chunk keep sets: keep sets")
+        want_keep = predictor.keep_sets(got, c.first_pos, c.B, wl.topk)
+        assert np.array_equal(keep, want_keep)
+    finally:
+        wl.close()

@@ -421,3 +421,35 @@ def test_score_rows_all_complete_reduces_to_score_blocks():
     s = predictor.score_rows(q, a, 10 * 4, 10)
     assert np.isfinite(s).all()
     assert np.allclose(s.max(axis=0), predictor.score_one(q, a), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------- partial last blocks
+
+def test_masked_score_brute_force():
+    rng = np.random.default_rng(21)
+    M, Hq, Hk, R, B, n = 2, 4, 2, 3, 4, 3
+    q = _rand_bits(rng, (M, Hq, R))
+    a = _rand_bits(rng, (n, Hk, B, R))
+    qd, ad = bf16.decode(q), bf16.decode(a)
+    for fill in range(0, B + 1):
+        got = predictor.score_one(q, a, fill)
+        for b in range(n):
+            toks = range(fill) if b == n - 1 else range(B)
+            vals = [sum(float(qd[i, h, j]) * float(ad[b, h // (Hq // Hk), t, j]) for j in range(R))
+                    for i in range(M) for h in range(Hq) for t in toks]
+            best = max(vals) if vals else -np.inf
+            assert got[b] == best or abs(got[b] - best) <= 1e-12 * max(1.0, abs(best)), (fill, b)
+
+
+def test_masked_score_equals_duplicated_tokens():
+    """Masking tokens t >= fill equals overwriting them with copies of token 0 (a max ignores duplicates)."""
+    rng = np.random.default_rng(8)
+    q = _rand_bits(rng, (3, 8, 16))
+    a = _rand_bits(rng, (6, 2, 8, 16))
+    assert np.array_equal(predictor.score_one(q, a, 8), predictor.score_one(q, a))
+    for fill in (1, 3, 7):
+        dup = a.copy()
+        dup[-1, :, fill:] = dup[-1, :, :1]
+        assert np.allclose(predictor.score_one(q, a, fill), predictor.score_one(q, dup), rtol=1e-12, atol=1e-12)
+    assert predictor.score_one(q, a, 0)[-1] == -np.inf
+    assert np.array_equal(predictor.score_one(q, a, 0)[:-1], predictor.score_one(q, a)[:-1])
