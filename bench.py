@@ -200,6 +200,43 @@ def main():
     tk = sorted(a.elapsed_time(b) for a, b in evk)
     breakdown[f"select_victims_k{k_sel}"] = round(tk[len(tk) // 2] * 1e3, 2)
 
+    # the whole step as one call (pred_decode_step) and as a replayed HIP graph of
+    # that call, against the four separate calls: host wall time per step over 30
+    # steps of the same layers (launch overhead shows where the GPU work is short)
+    l0f = wl.layer0_for_step(0)
+    qp_f, sc_f, vic_f = torch.empty_like(wl.q_proj), torch.empty_like(wl.scores), torch.empty_like(wl.victims)
+
+    def fused():
+        rk.pred_decode_step(wl.h, l0f, wl.k_new[l0f:l0f + nl], wl.table_new[l0f:l0f + nl], wl.q[l0f:l0f + nl],
+                            qp_f, wl.tables, None, sc_f, c.n, vic_f, wl.workspace)
+
+    def separate():
+        rk.pred_project_kv_block(wl.h, l0f, wl.k_new[l0f:l0f + nl], wl.table_new[l0f:l0f + nl])
+        rk.pred_project_q(wl.h, wl.q[l0f:l0f + nl], qp_f)
+        rk.pred_score_blocks(wl.h, l0f, qp_f, wl.tables, sc_f)
+        rk.pred_rank_victims(wl.h, sc_f.view(nl * c.S, c.n), vic_f, wl.workspace)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        fused()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fused()
+    fused_us = {}
+    for name, fn in (("separate_calls", separate), ("decode_step", fused), ("graph_replay", graph.replay)):
+        fn()
+        torch.cuda.synchronize()
+        t_a = time.perf_counter()
+        for _ in range(30):
+            fn()
+        torch.cuda.synchronize()
+        fused_us[name] = round((time.perf_counter() - t_a) / 30 * 1e6, 2)
+    del graph
+    rk.pred_device_error(wl.h)
+
     # per-row causal scores and keep sets of the first layer and sequence (many-row
     # workloads): each query row against the blocks complete at its position, then
     # every row's top-k; timed per entry point, median of 20
@@ -299,6 +336,7 @@ def main():
     out["step_breakdown_median_us"] = breakdown
     if per_layer is not None:
         out["score_per_layer_call"] = per_layer
+    out["step_wall_us"] = fused_us
     if keep_sets is not None:
         out["keep_sets"] = keep_sets
     if not args.no_cpu_baseline:

@@ -227,6 +227,30 @@ int pred_select_keep(pred_t* p, const float* scores, int64_t rows, int64_t strid
                      int32_t ratio, int64_t topk, int32_t* keep, void* workspace, size_t ws_bytes,
                      void* stream);
 
+/* One decode step in one call: the step's new blocks into A_g, q_proj of every
+ * layer, block scores and each (layer, sequence) row's k lowest blocks in
+ * eviction order -- pred_project_kv_block, pred_project_q,
+ * pred_score_blocks_masked and pred_select_victims (pred_rank_victims when
+ * k = n_blocks) on one stream, in that order, with the same arguments and
+ * results (predictor.rs page: project_q, project_kv_block and score_blocks of
+ * one step; module doc: the scores rank eviction victims).
+ *   k_new       device, [n_layers, n_new, block_size, num_kv_heads, head_dim] bf16
+ *   new_table   device, [n_layers, n_new] int32 slots for them (NULL: 0..n_new-1)
+ *   q           device, [n_layers, n_seqs, n_rows, num_q_heads, head_dim] bf16
+ *   q_proj      device, [n_layers, n_seqs, n_rows, num_q_heads, r] bf16 output
+ *   block_tables, n_blocks, n_seqs, last_fill: as for pred_score_blocks_masked
+ *   scores      device, [n_layers, n_seqs, n_blocks] float32 output
+ *   victims     device, [n_layers * n_seqs, k] int32 output, 0 <= k <= n_blocks
+ *   workspace   pred_rank_workspace_bytes(n_blocks, n_layers * n_seqs) bytes
+ * Every part's arguments are checked before anything is enqueued.  The step
+ * allocates nothing, never synchronises and issues no memset, so a caller may
+ * capture it into a HIP graph and replay it (the arguments are then fixed). */
+int pred_decode_step(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* k_new,
+                     const int32_t* new_table, int64_t n_new, const pred_bf16* q, int32_t n_rows,
+                     pred_bf16* q_proj, const int32_t* block_tables, int64_t n_blocks, int32_t n_seqs,
+                     const int32_t* last_fill, float* scores, int64_t k, int32_t* victims,
+                     void* workspace, size_t ws_bytes, void* stream);
+
 /* Workspace pred_rank_victims needs for this shape: 0 for n_blocks <= 2048
  * (each segment is sorted inside one workgroup), else 8 bytes per key for the
  * sorted runs, twice that for n_blocks > 8192 (pairwise merge buffers). */

@@ -242,6 +242,43 @@ def pred_select_keep(h, scores, first_pos, ratio, topk, keep, workspace=None, st
                                   ws_bytes, _stream(stream)))
 
 
+def pred_decode_step(h, layer0, k_new, new_table, q, q_proj, block_tables, last_fill, scores, k, victims,
+                     workspace=None, stream=None):
+    """One decode step: k_new [n_layers, n_new, B, Hk, D] (+ new_table [n_layers, n_new] or None) into A_g,
+    q [n_layers, n_seqs, n_rows, Hq, D] -> q_proj, scores [n_layers, n_seqs, n_blocks], victims
+    [n_layers * n_seqs, k] (the k lowest of each row in eviction order)."""
+    import torch
+    d = pred_get_dims(h)
+    bt = _bf16_types()
+    if q.dim() != 5 or tuple(q.shape[3:]) != (d.num_q_heads, d.head_dim):
+        raise ValueError(f"q must be [n_layers, n_seqs, n_rows, {d.num_q_heads}, {d.head_dim}]")
+    n_layers, n_seqs, n_rows = q.shape[:3]
+    if tuple(q_proj.shape) != (n_layers, n_seqs, n_rows, d.num_q_heads, d.r):
+        raise ValueError("q_proj must be [n_layers, n_seqs, n_rows, num_q_heads, r]")
+    if k_new.dim() != 5 or k_new.shape[0] != n_layers or tuple(k_new.shape[2:]) != (d.block_size, d.num_kv_heads,
+                                                                                    d.head_dim):
+        raise ValueError("k_new must be [n_layers, n_new, block_size, num_kv_heads, head_dim]")
+    n_new = k_new.shape[1]
+    if new_table is not None and tuple(new_table.shape) != (n_layers, n_new):
+        raise ValueError("new_table must be [n_layers, n_new]")
+    if scores.dim() != 3 or tuple(scores.shape[:2]) != (n_layers, n_seqs):
+        raise ValueError("scores must be [n_layers, n_seqs, n_blocks]")
+    n_blocks = scores.shape[2]
+    if block_tables is not None and tuple(block_tables.shape) != (n_seqs, n_blocks):
+        raise ValueError("block_tables must be [n_seqs, n_blocks]")
+    if last_fill is not None and tuple(last_fill.shape) != (n_seqs,):
+        raise ValueError("last_fill must be [n_seqs]")
+    if tuple(victims.shape) != (n_layers * n_seqs, k):
+        raise ValueError("victims must be [n_layers * n_seqs, k]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pred_decode_step(h, layer0, n_layers, _ptr(k_new, "k_new", bt),
+                                  _ptr(new_table, "new_table", (torch.int32,)), n_new, _ptr(q, "q", bt), n_rows,
+                                  _ptr(q_proj, "q_proj", bt), _ptr(block_tables, "block_tables", (torch.int32,)),
+                                  n_blocks, n_seqs, _ptr(last_fill, "last_fill", (torch.int32,)),
+                                  _ptr(scores, "scores", (torch.float32,)), k, _ptr(victims, "victims", (torch.int32,)),
+                                  _ptr(workspace, "workspace"), ws_bytes, _stream(stream)))
+
+
 # ------------------------------------------------------------------ inspection
 
 def pred_copy_projection(h):

@@ -67,6 +67,8 @@ SIGNATURES = {
     "pred_select_victims": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp]),
     "pred_score_rows": (ctypes.c_int, [_vp, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
     "pred_select_keep": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp, _vp, ctypes.c_size_t, _vp]),
+    "pred_decode_step": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i64, _i32, _vp,
+                                         _vp, _i64, _vp, _vp, ctypes.c_size_t, _vp]),
     "pred_rank_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "pred_projection_host": (ctypes.c_int, [_i32, _i32, _u64, _vp]),
     "pred_copy_projection": (ctypes.c_int, [_vp, _vp]),

@@ -64,6 +64,8 @@ const char* score_rows_path_name(const RowScoreArgs& a);
 
 // ---- ranking (rank.hip) --------------------------------------------------
 size_t rank_workspace_bytes(int64_t n, int64_t n_seg);
+// Per-device set-up of the ranking kernels (their LDS limits); called by pred_create.
+hipError_t rank_prepare();
 // Sort order of a ranking row.  Ascending (eviction order): the order key of
 // the score, NaN first.  Descending (a keep set, larger score first): keys
 // flipped inside [0, 0xFF800001] so that they stay below the padding key and

@@ -131,6 +131,7 @@ int create_impl(const pred_dims* d, const uint16_t* p_host_in, uint64_t seed, ui
         delete p;
         return code;
     };
+    if ((e = pred::rank_prepare()) != hipSuccess) return cleanup(hip_fail(e, "ranking kernel set-up"));
     if ((e = hipMalloc(&p->p_dev, (size_t)pn * 2)) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(P)"));
     if ((e = hipMalloc(&p->pf_dev, (size_t)pn * 8)) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(P f64)"));
     if ((e = hipMalloc(&p->err_dev, 4)) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(error word)"));
@@ -215,7 +216,12 @@ void pred_destroy(pred_t* p) {
     delete p;
 }
 
-int pred_project_q(pred_t* p, const pred_bf16* q, int64_t n_vec, pred_bf16* q_proj, void* stream) {
+// Every entry point's work is an impl(..., go): all host checks first, and with
+// go == false it returns after them, so a composite call (pred_decode_step)
+// can check every part before it enqueues anything.
+namespace {
+
+int project_q_impl(pred_t* p, const pred_bf16* q, int64_t n_vec, pred_bf16* q_proj, void* stream, bool go) {
     if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
     if (n_vec < 0) return fail(PRED_ERR_OUT_OF_RANGE, "n_vec (%lld) < 0", (long long)n_vec);
     if (n_vec == 0) return ok();
@@ -223,13 +229,14 @@ int pred_project_q(pred_t* p, const pred_bf16* q, int64_t n_vec, pred_bf16* q_pr
     if (!aligned16(q) || !aligned16(q_proj)) return fail(PRED_ERR_UNSUPPORTED, "q and q_proj must be 16-byte aligned");
     int64_t rows;
     if (!mul_ok(n_vec, p->d.num_q_heads, &rows)) return fail(PRED_ERR_OUT_OF_RANGE, "n_vec too large");
+    if (!go) return ok();
     hipError_t e = pred::launch_project_dense(q, p->pf_dev, q_proj, rows, p->d.head_dim, p->d.r, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "project_q launch");
     return ok();
 }
 
-int pred_project_kv_block(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* k,
-                          const int32_t* block_table, int64_t n_blocks, void* stream) {
+int project_kv_impl(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* k, const int32_t* block_table,
+                    int64_t n_blocks, void* stream, bool go) {
     if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
     if (layer0 < 0 || n_layers < 0 || (int64_t)layer0 + n_layers > p->d.num_layers)
         return fail(PRED_ERR_OUT_OF_RANGE, "project_kv_block out of range: layers [%d, %d) of %d", layer0,
@@ -241,6 +248,7 @@ int pred_project_kv_block(pred_t* p, int32_t layer0, int32_t n_layers, const pre
     if (n_blocks == 0 || n_layers == 0) return ok();
     if (!k) return fail(PRED_ERR_NULL_ARG, "k is NULL");
     if (!aligned16(k)) return fail(PRED_ERR_UNSUPPORTED, "k must be 16-byte aligned");
+    if (!go) return ok();
     const pred_dims& d = p->d;
     uint16_t* a_first = p->ag_dev + (int64_t)layer0 * d.max_blocks * d.num_kv_heads * d.block_size * d.r;
     hipError_t e = pred::launch_project_paged(k, p->pf_dev, a_first, block_table, n_layers, n_blocks, d.max_blocks,
@@ -250,11 +258,9 @@ int pred_project_kv_block(pred_t* p, int32_t layer0, int32_t n_layers, const pre
     return ok();
 }
 
-namespace {
-
 int score_impl(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* q_proj, int32_t n_rows,
                const int32_t* block_tables, int64_t n_blocks, int32_t n_seqs, const int32_t* last_fill,
-               float* scores, void* stream) {
+               float* scores, void* stream, bool go) {
     if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
     if (layer0 < 0 || n_layers < 0 || (int64_t)layer0 + n_layers > p->d.num_layers)
         return fail(PRED_ERR_OUT_OF_RANGE, "score_blocks layers [%d, %d) outside [0, %d)", layer0, layer0 + n_layers,
@@ -269,6 +275,7 @@ int score_impl(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* q_p
     if (n_rows == 0) return fail(PRED_ERR_OUT_OF_RANGE, "n_rows must be >= 1");
     if (!q_proj || !scores) return fail(PRED_ERR_NULL_ARG, "q_proj or scores is NULL");
     if (!aligned16(q_proj)) return fail(PRED_ERR_UNSUPPORTED, "q_proj must be 16-byte aligned");
+    if (!go) return ok();
     pred::ScoreArgs a;
     a.qp = q_proj;
     a.ag = p->ag_dev;
@@ -296,16 +303,26 @@ int score_impl(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* q_p
 
 }  // namespace
 
+int pred_project_q(pred_t* p, const pred_bf16* q, int64_t n_vec, pred_bf16* q_proj, void* stream) {
+    return project_q_impl(p, q, n_vec, q_proj, stream, true);
+}
+
+int pred_project_kv_block(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* k,
+                          const int32_t* block_table, int64_t n_blocks, void* stream) {
+    return project_kv_impl(p, layer0, n_layers, k, block_table, n_blocks, stream, true);
+}
+
 int pred_score_blocks(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* q_proj, int32_t n_rows,
                       const int32_t* block_tables, int64_t n_blocks, int32_t n_seqs, float* scores, void* stream) {
-    return score_impl(p, layer0, n_layers, q_proj, n_rows, block_tables, n_blocks, n_seqs, nullptr, scores, stream);
+    return score_impl(p, layer0, n_layers, q_proj, n_rows, block_tables, n_blocks, n_seqs, nullptr, scores, stream,
+                      true);
 }
 
 int pred_score_blocks_masked(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* q_proj, int32_t n_rows,
                              const int32_t* block_tables, int64_t n_blocks, int32_t n_seqs, const int32_t* last_fill,
                              float* scores, void* stream) {
     return score_impl(p, layer0, n_layers, q_proj, n_rows, block_tables, n_blocks, n_seqs, last_fill, scores,
-                      stream);
+                      stream, true);
 }
 
 int pred_score_rows(pred_t* p, int32_t layer, const pred_bf16* q_proj, int64_t rows, int64_t first_pos,
@@ -352,7 +369,7 @@ namespace {
 // The k lowest of every segment, in eviction order; k = n_blocks is the full ranking.
 int rank_or_select(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments, int64_t k,
                    pred::RowOrder ro, int32_t* victims, void* workspace, size_t ws_bytes, void* stream,
-                   const char* what) {
+                   const char* what, bool go = true) {
     if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
     if (n_blocks < 0 || n_segments < 0)
         return fail(PRED_ERR_OUT_OF_RANGE, "negative count (n_blocks %lld, n_segments %lld)", (long long)n_blocks,
@@ -368,6 +385,7 @@ int rank_or_select(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_s
         return fail(PRED_ERR_WORKSPACE, "%s needs a %zu-byte workspace (%zu given)", what, need,
                     workspace ? ws_bytes : (size_t)0);
     if (need > 0 && ((uintptr_t)workspace & 7u)) return fail(PRED_ERR_WORKSPACE, "workspace must be 8-byte aligned");
+    if (!go) return ok();
     hipError_t e = pred::launch_rank(scores, n_blocks, n_segments, k, ro, victims, workspace, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, what);
     return ok();
@@ -395,6 +413,33 @@ int pred_select_keep(pred_t* p, const float* scores, int64_t rows, int64_t strid
         return fail(PRED_ERR_OUT_OF_RANGE, "first_pos (%lld) outside [0, 2^62]", (long long)first_pos);
     return rank_or_select(p, scores, stride, rows, topk, pred::RowOrder{1, first_pos, ratio}, keep, workspace,
                           ws_bytes, stream, "select_keep");
+}
+
+int pred_decode_step(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* k_new, const int32_t* new_table,
+                     int64_t n_new, const pred_bf16* q, int32_t n_rows, pred_bf16* q_proj,
+                     const int32_t* block_tables, int64_t n_blocks, int32_t n_seqs, const int32_t* last_fill,
+                     float* scores, int64_t k, int32_t* victims, void* workspace, size_t ws_bytes, void* stream) {
+    if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
+    if (n_layers < 0 || n_seqs < 0 || n_rows < 0)
+        return fail(PRED_ERR_OUT_OF_RANGE, "negative count (n_layers %d, n_seqs %d, n_rows %d)", n_layers, n_seqs,
+                    n_rows);
+    int64_t n_vec, n_seg;
+    if (!mul_ok((int64_t)n_layers * n_seqs, n_rows, &n_vec) || !mul_ok(n_layers, n_seqs, &n_seg))
+        return fail(PRED_ERR_OUT_OF_RANGE, "decode_step: too many rows");
+    // every part is checked before anything is enqueued
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool go = pass == 1;
+        int rc = project_kv_impl(p, layer0, n_layers, k_new, new_table, n_new, stream, go);
+        if (rc == 0) rc = project_q_impl(p, q, n_vec, q_proj, stream, go);
+        if (rc == 0)
+            rc = score_impl(p, layer0, n_layers, q_proj, n_rows, block_tables, n_blocks, n_seqs, last_fill, scores,
+                            stream, go);
+        if (rc == 0)
+            rc = rank_or_select(p, scores, n_blocks, n_seg, k, pred::RowOrder{0, 0, 0}, victims, workspace, ws_bytes,
+                                stream, "decode_step ranking", go);
+        if (rc) return rc;
+    }
+    return ok();
 }
 
 size_t pred_rank_workspace_bytes(int64_t n_blocks, int64_t n_segments) {

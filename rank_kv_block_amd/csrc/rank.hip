@@ -311,18 +311,22 @@ template <int RL, int G, int TPB>
 hipError_t launch_count_merge(const uint32_t* ik, const uint32_t* ii, int64_t n, int64_t n_seg, int64_t klim,
                               int64_t vstride, int32_t* victims, uint32_t* ok, uint32_t* oi, hipStream_t st) {
     const int nruns = (int)((n + RL - 1) / RL);
-    const size_t lds = (size_t)G * RL * sizeof(uint32_t);
-    if (lds > 65536) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rank_count_merge_kernel<RL, G, TPB>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    const size_t lds = (size_t)G * RL * sizeof(uint32_t);   // above 64 KiB: allowed by rank_prepare
     rank_count_merge_kernel<RL, G, TPB><<<(unsigned)(n_seg * nruns * (RL / TPB)), TPB, lds, st>>>(
         ik, ii, n, nruns, klim, vstride, victims, ok, oi);
     return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t rank_prepare() {
+    // the second merge level keeps 128 KiB of keys in LDS; set once per device
+    // at handle creation, so a ranking call makes no attribute call (it can be
+    // captured into a graph)
+    return hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&rank_count_merge_kernel<kMaxLdsItems, kMaxGroup2 / kMaxLdsItems, kMergeTPB>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kMaxGroup2 * sizeof(uint32_t)));
+}
 
 size_t rank_workspace_bytes(int64_t n, int64_t n_seg) {
     if (n <= kSingle || n_seg <= 0) return 0;
