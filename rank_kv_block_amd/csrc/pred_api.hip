@@ -187,7 +187,8 @@ const char* pred_limits(void) {
            "other shapes use a plain per-block kernel. Rank: n_blocks <= 2^31-1; above 2048 per segment a "
            "workspace of 8*n_blocks*n_segments bytes is needed (16*n_blocks*n_segments above 8192); select_keep "
            "the same with n_blocks = stride, n_segments = rows. Row scorer: MFMA for r in {16,32,64,128}, "
-           "block_size in {8,16,32}, num_kv_heads in {1,2,4,8}, num_kv_heads*r <= 512; a plain kernel otherwise.";
+           "block_size in {8,16,32}, num_kv_heads in {1,2,4,8}, num_q_heads a multiple of 4; a plain kernel "
+           "otherwise.";
 }
 
 const char* pred_version(void) { return "rank_kv_block_amd 0.1 (gfx950)"; }

@@ -9,44 +9,70 @@
 // complete(r) <= b < stride.  A complete block whose table entry is outside
 // [0, max_blocks) scores NaN and raises the device error word.
 //
-// Per row tile the contraction is Q_h [32 rows, R] x A_kv(h)^T [R, 32 keys] for
-// every query head h, on v_mfma_f32_32x32x16_bf16 with f32 accumulation.  A wave
-// keeps NKT tiles of 32 keys (consecutive tokens of consecutive blocks) of every
-// kv head in registers as B operands, so a row's max over heads is an
-// elementwise max of the heads' accumulators: the same lane and element hold
-// the same (row, key) for every head.  Query vectors stream through LDS in
-// stages of 32 rows x 4 heads, double-buffered: all 256 threads load the next
-// stage with coalesced 16-byte reads while the current one is multiplied, and
-// the waves read their A operands from LDS in the MFMA layout (vectors padded by
-// 16 bytes so the rows of one read fall in distinct banks).  After a row tile's
-// last head each lane reduces its key column's 16 rows over the B lanes of its
-// block, and one lane per block writes the 16 row scores.
+// Per row tile of 32 rows the contraction is A_kv(h) [32 keys, R] x Q_h^T [R,
+// 32 rows] for every query head h, on v_mfma_f32_32x32x16_bf16 with f32
+// accumulation (keys as the A operand, so a lane holds one query row and 16
+// keys of the tile: element i is key (i / 4) * 8 + 4 * (lane / 32) + i % 4).
+// The four waves of a workgroup share one range of NKT tiles of 32 keys
+// (consecutive tokens of consecutive blocks) and split the query heads: wave w
+// takes heads [w * Hq / 4, (w + 1) * Hq / 4), whose one or two kv heads' keys
+// it keeps in registers.  Each query operand read from LDS then serves NKT
+// tiles.  After every head a lane folds its 16 products into the running
+// maxima of the tile's blocks (B / 2 elements per block, max3 chains); after a
+// row tile the two lane halves are combined, the four waves' partial maxima
+// meet in LDS and the workgroup writes each row's blocks with stores that run
+// along the row.
 //
-// Causality: the key tiles of a wave that start at or past the last row's
-// complete blocks skip their MFMAs (all their scores are -inf); tiles are in key
-// order, so the ones still needed are a prefix.
+// Query vectors stream through LDS in stages of 32 rows x (4 waves x SH heads),
+// double-buffered: all 256 threads load the next stage with 16-byte reads while
+// the current one is multiplied, and each wave reads its own heads' vectors in
+// the MFMA layout (vectors padded by 16 bytes so the rows of one read fall in
+// distinct banks).
 //
-// Workgroups are (key group of 4 waves x NKT tiles) x (row part) with the row
-// part fastest: with 4 or 8 parts every XCD (each takes every 8th workgroup)
-// serves one or two parts, and its L2 holds only those parts' queries.
+// Causality: key tiles that start at or past the last row's complete blocks
+// skip their MFMAs (their scores are all -inf); tiles are in key order, so the
+// ones still needed are a prefix, the same for every wave.
+//
+// A workgroup holds PRED_ROWS_KG key groups of four waves that share each query
+// stage.  Workgroups are (key range) x (row part) with the row part fastest:
+// with 4 or 8 parts every XCD (each takes every 8th workgroup) serves one or
+// two parts, and its L2 holds only those parts' queries.
 #include "common.h"
 #include "kernels.h"
+
+// Tuning knobs (compile-time), each measured on the 2048-row prefill chunk
+// (r = 64, 8 kv heads): 96 key registers (3 tiles) keep two waves per SIMD
+// (128 registers: 4 tiles, one wave, 580 us; 96: 455 us); 8192 target waves
+// give 8 row parts there, so an XCD's L2 holds one part's 1 MiB of queries
+// (444 us); two key groups per workgroup share each query stage, halving the
+// query reads (427-440 us).  Two-head stages at r = 64 measured no better.
+#ifndef PRED_ROWS_TARGET_WAVES
+#define PRED_ROWS_TARGET_WAVES 8192
+#endif
+// key groups per workgroup: KG groups of four waves share each query stage
+#ifndef PRED_ROWS_KG
+#define PRED_ROWS_KG 2
+#endif
+// stages of two heads per wave for r up to this (one head above)
+#ifndef PRED_ROWS_SH2_MAX_R
+#define PRED_ROWS_SH2_MAX_R 32
+#endif
 
 namespace pred {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kStageHeads = 4;                    // query heads per LDS stage
-constexpr int kStageVecs = 32 * kStageHeads;      // query vectors per stage
-constexpr int64_t kTargetWaves = 2048;            // two per SIMD
+constexpr int kWaves = 4;                         // waves of one key group (they split the heads)
+constexpr int kKG = PRED_ROWS_KG;
+constexpr int kThreads = 256 * kKG;
+constexpr int64_t kTargetWaves = PRED_ROWS_TARGET_WAVES;
 
 struct RowGeom {
-    int64_t groups;       // key groups (kWaves * NKT * 32 keys each)
+    int64_t groups;       // workgroups along the keys (kKG * NKT * 32 keys each)
     int row_tiles;        // ceil(rows / 32)
     int parts;            // row parts
     int tiles_per_part;
-    int stages;           // ceil(Hq / 4) stages per row tile
+    int stages;           // stages per row tile: (Hq / 4) / SH
 };
 
 __device__ inline int64_t complete_blocks(const RowScoreArgs& a, int64_t r) {
@@ -54,169 +80,172 @@ __device__ inline int64_t complete_blocks(const RowScoreArgs& a, int64_t r) {
     return c < a.n ? c : a.n;
 }
 
-// R: projected width; HK: kv heads (keys of all of them sit in registers);
-// NKT: 32-key tiles per wave.
-template <int R, int HK, int NKT>
-__global__ __launch_bounds__(256) void score_rows_kernel(RowScoreArgs a, RowGeom gm) {
+// R: projected width; KPW: kv heads per wave (2 when Hk = 8, else 1); NKT:
+// 32-key tiles per wave; SH: heads per wave per stage; BS: block size.
+template <int R, int KPW, int NKT, int SH, int BS>
+__global__ __launch_bounds__(kThreads) void score_rows_kernel(RowScoreArgs a, RowGeom gm) {
     constexpr int RS = R / 16;                        // MFMA k-steps of 16
     constexpr int CPR = R / 8;                        // 16-byte pieces per query vector
     constexpr int ROWB = R * 2 + 16;                  // LDS bytes per query vector
-    constexpr int PIECES = kStageVecs * CPR;          // 16-byte pieces per stage
-    constexpr int PPT = (PIECES + 255) / 256;         // pieces per thread
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2][kStageVecs * ROWB];
+    constexpr int VEC = 32 * kWaves * SH;             // query vectors per stage
+    constexpr int PIECES = VEC * CPR;                 // 16-byte pieces per stage
+    constexpr int PPT = (PIECES + kThreads - 1) / kThreads;   // pieces per thread
+    constexpr bool kFull = PIECES % kThreads == 0;            // every thread has PPT pieces
+    constexpr int BPT = 32 / BS;                      // blocks per key tile
+    constexpr int EPB = BS / 2;                       // accumulator elements per block in a lane
+    constexpr int NB = NKT * BPT;                     // blocks of a key group
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2][VEC * ROWB];
+    __shared__ float red[kKG][kWaves][NB * 32];       // partial maxima [key group][wave][block][row]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = (tid >> 6) % kWaves;             // head quarter
+    const int kg = (tid >> 6) / kWaves;               // key group of this wave
     const int part = (int)(blockIdx.x % gm.parts);
     const int64_t grp = blockIdx.x / gm.parts;
     const int rt_begin = part * gm.tiles_per_part;
     const int rt_end = (rt_begin + gm.tiles_per_part) < gm.row_tiles ? (rt_begin + gm.tiles_per_part) : gm.row_tiles;
     if (rt_begin >= rt_end) return;   // whole workgroup
-    const int g = a.Hq / HK;
-    const int col = lane & 31;        // key column of a tile / query row of a tile
+    const int qh = a.Hq / kWaves;     // heads per wave
+    const int g = a.Hq / a.Hk;
+    const int kv_first = (wave * qh) / g;
+    const int col = lane & 31;        // key of a tile (A operand) / query row (B operand)
     const int half = lane >> 5;       // which 8 of the 16 k-values of one MFMA step
-    const int64_t n_keys = a.n * a.B;
-    const int64_t key0 = (grp * kWaves + wave) * (NKT * 32);
-    const int64_t slot_elems = (int64_t)HK * a.B * R;
+    const int64_t n_keys = a.n * BS;
+    const int64_t key0 = (grp * kKG + kg) * (NKT * 32);
+    const int64_t slot_elems = (int64_t)a.Hk * BS * R;
 
-    // B operands: this lane's key column of every tile and kv head.
-    bf16x8_t kb[NKT][HK][RS];
-    uint32_t live = 0;
+    // A operands: this lane's key of every tile, for the wave's kv heads.
+    bf16x8_t kb[NKT][KPW][RS];
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
         const int64_t key = key0 + t * 32 + col;
-        const uint16_t* src = a.ag;   // in bounds for lanes without a key; never used then
+        const uint16_t* src = a.ag;   // in bounds for lanes without a valid key; their blocks are never stored
         if (key < n_keys) {
-            const int64_t b = key / a.B;
-            const int tok = (int)(key - b * a.B);
+            const int64_t b = key / BS;
+            const int tok = (int)(key - b * BS);
             const int64_t phys = a.table ? (int64_t)a.table[b] : b;
-            if (phys >= 0 && phys < a.N) {
-                src = a.ag + (a.layer * a.N + phys) * slot_elems + (int64_t)tok * R;
-                live |= 1u << t;
-            }
+            if (phys >= 0 && phys < a.N) src = a.ag + (a.layer * a.N + phys) * slot_elems + (int64_t)tok * R;
         }
 #pragma unroll
-        for (int k = 0; k < HK; ++k)
+        for (int k = 0; k < KPW; ++k) {
+            const int kv = (kv_first + k) < a.Hk ? kv_first + k : a.Hk - 1;
 #pragma unroll
-            for (int st = 0; st < RS; ++st) kb[t][k][st] = load8(src + (int64_t)k * a.B * R + st * 16 + half * 8);
+            for (int st = 0; st < RS; ++st) kb[t][k][st] = load8(src + (int64_t)kv * BS * R + st * 16 + half * 8);
+        }
     }
 
-    f32x16_t rm[NKT];
+    float rm[NKT][BPT];
 #pragma unroll
     for (int t = 0; t < NKT; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) rm[t][i] = -__builtin_inff();
+        for (int bi = 0; bi < BPT; ++bi) rm[t][bi] = -__builtin_inff();
 
-    // stage (row tile rt, heads 4s..4s+3): piece p -> row p / (4 * CPR), head
-    // (p / CPR) % 4, piece p % CPR; global reads run along a row's four heads,
-    // LDS holds the stage head-major ([head][row]) for the MFMA reads
-    // (plain functions of the piece index, so the prefetch registers stay registers)
+    // stage (row tile rt, stage s): vector v = row * (4 SH) + slot, slot = wave * SH + j,
+    // holding head wave * qh + s * SH + j of that row; LDS keeps it at slot * 32 + row
     u32x4_t gq[PPT];
     auto piece_src = [&](int rt, int s, int p) -> const u32x4_t* {
-        const int hv = p / CPR;
-        int64_t r = (int64_t)rt * 32 + hv / kStageHeads;
+        const int v = p / CPR;
+        const int slot = v % (kWaves * SH);
+        int64_t r = (int64_t)rt * 32 + v / (kWaves * SH);
         if (r >= a.rows) r = a.rows - 1;   // padding rows repeat a real row
-        int h = s * kStageHeads + hv % kStageHeads;
-        if (h >= a.Hq) h = a.Hq - 1;       // padding heads are never multiplied
+        const int h = (slot / SH) * qh + s * SH + slot % SH;
         return reinterpret_cast<const u32x4_t*>(a.qp + (r * a.Hq + h) * R + (p % CPR) * 8);
     };
     auto piece_dst = [&](int buf, int p) -> u32x4_t* {
-        const int hv = p / CPR;
-        const int vec = (hv % kStageHeads) * 32 + hv / kStageHeads;
+        const int v = p / CPR;
+        const int vec = (v % (kWaves * SH)) * 32 + v / (kWaves * SH);
         return reinterpret_cast<u32x4_t*>(&lds[buf][vec * ROWB + (p % CPR) * 16]);
     };
-    // the stage's heads against this wave's first ntl key tiles; the keys of
-    // kv head k are registers, so k is unrolled and its heads of the stage
-    // (those with h / g == k) run as a loop
+    // this wave's heads of stage s against its first ntl key tiles
     auto stage_mfma = [&](int buf, int s, int ntl) {
-        const int h0 = s * kStageHeads;
-        const int h_end = (h0 + kStageHeads) < a.Hq ? (h0 + kStageHeads) : a.Hq;
 #pragma unroll
-        for (int k = 0; k < HK; ++k) {
-            const int lo = h0 > k * g ? h0 : k * g;
-            const int hi = h_end < (k + 1) * g ? h_end : (k + 1) * g;
-            for (int h = lo; h < hi; ++h) {   // wave-uniform bounds
-                bf16x8_t qa[RS];
+        for (int j = 0; j < SH; ++j) {
+            const int h = wave * qh + s * SH + j;
+            const int lk = h / g - kv_first;   // which of the wave's kv heads (wave-uniform)
+            bf16x8_t qb[RS];
 #pragma unroll
-                for (int st = 0; st < RS; ++st)
-                    qa[st] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                            &lds[buf][((h - h0) * 32 + col) * ROWB + (st * 2 + half) * 16]));
-                f32x16_t acc[NKT];
+            for (int st = 0; st < RS; ++st)
+                qb[st] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                        &lds[buf][((wave * SH + j) * 32 + col) * ROWB + (st * 2 + half) * 16]));
+#pragma unroll
+            for (int k = 0; k < KPW; ++k) {
+                if (KPW > 1 && k != lk) continue;
+                // each tile's chain, then its fold: the fold of tile t overlaps the
+                // chain of tile t + 1, and only two accumulators are live
 #pragma unroll
                 for (int t = 0; t < NKT; ++t) {
                     if (t < ntl) {
-                        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0], kb[t][k][0], f32x16_t{}, 0, 0, 0);
+                        f32x16_t acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[t][k][0], qb[0], f32x16_t{}, 0, 0, 0);
 #pragma unroll
                         for (int st = 1; st < RS; ++st)
-                            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], kb[t][k][st], acc[t], 0, 0, 0);
+                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[t][k][st], qb[st], acc, 0, 0, 0);
+#pragma unroll
+                        for (int bi = 0; bi < BPT; ++bi) {
+                            float m = rm[t][bi];
+#pragma unroll
+                            for (int e = 0; e < EPB; e += 2) m = fmaxf(m, fmaxf(acc[bi * EPB + e], acc[bi * EPB + e + 1]));
+                            rm[t][bi] = m;
+                        }
                     }
                 }
-#pragma unroll
-                for (int t = 0; t < NKT; ++t)
-                    if (t < ntl)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) rm[t][i] = fmaxf(rm[t][i], acc[t][i]);
             }
         }
     };
-    // row tile rt done: block maxima of every row, written out; rm reset
+    // row tile rt done: combine the lane halves and the waves, store, reset
     auto epilogue = [&](int rt) {
-        const int64_t r0 = (int64_t)rt * 32;
 #pragma unroll
-        for (int t = 0; t < NKT; ++t) {
-            // element i of the accumulator is row (i / 4) * 8 + half * 4 + i % 4 of the tile
+        for (int t = 0; t < NKT; ++t)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float v = fmaxf(rm[t][i], lane_xor<1>(rm[t][i]));
-                rm[t][i] = fmaxf(v, lane_xor<2>(v));
+            for (int bi = 0; bi < BPT; ++bi) {
+                const float v = fmaxf(rm[t][bi], lane_xor<32>(rm[t][bi]));
+                if (half == 0) red[kg][wave][(t * BPT + bi) * 32 + col] = v;
+                rm[t][bi] = -__builtin_inff();
             }
-            if (a.B >= 8)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) rm[t][i] = fmaxf(rm[t][i], lane_xor<7>(rm[t][i]));
-            if (a.B >= 16)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) rm[t][i] = fmaxf(rm[t][i], lane_xor<15>(rm[t][i]));
-            if (a.B >= 32)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) rm[t][i] = fmaxf(rm[t][i], lane_xor<16>(rm[t][i]));
-            const int64_t key = key0 + t * 32 + col;
-            if ((col % a.B) == 0 && key < n_keys) {
-                const int64_t b = key / a.B;
-                const bool ok = (live >> t) & 1u;
-                bool bad = false;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int64_t r = r0 + (i / 4) * 8 + half * 4 + (i % 4);
-                    if (r < a.rows) {
-                        const bool inside = b < complete_blocks(a, r);
-                        bad |= inside && !ok;
-                        a.scores[r * a.stride + b] =
-                            inside ? (ok ? rm[t][i] : __uint_as_float(0x7FC00000u)) : -__builtin_inff();
+        __syncthreads();
+        const int64_t r0 = (int64_t)rt * 32;
+        const int64_t blk0 = grp * kKG * NB;          // first block of the workgroup
+        for (int i = tid; i < kKG * NB * 32; i += kThreads) {
+            const int row = i / (kKG * NB);           // consecutive threads: consecutive blocks of a row
+            const int bw = i - row * (kKG * NB);
+            const int g2 = bw / NB;
+            const int blk = bw - g2 * NB;
+            const int64_t r = r0 + row;
+            const int64_t b = blk0 + bw;
+            if (r < a.rows && b < a.n) {
+                float v = fmaxf(fmaxf(red[g2][0][blk * 32 + row], red[g2][1][blk * 32 + row]),
+                                fmaxf(red[g2][2][blk * 32 + row], red[g2][3][blk * 32 + row]));
+                if (b >= complete_blocks(a, r)) {
+                    v = -__builtin_inff();
+                } else if (a.table) {
+                    const int64_t phys = a.table[b];
+                    if (phys < 0 || phys >= a.N) {
+                        v = __uint_as_float(0x7FC00000u);
+                        atomicOr(a.err, DEVERR_TABLE);
                     }
                 }
-                if (bad) atomicOr(a.err, DEVERR_TABLE);
+                a.scores[r * a.stride + b] = v;
             }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) rm[t][i] = -__builtin_inff();
         }
+        // red is written again only after the next row tile's stage barriers
     };
 
-    static_assert(PIECES % 256 == 0, "whole pieces per thread");
     int buf = 0;
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) gq[i] = *piece_src(rt_begin, 0, tid + 256 * i);
+    for (int i = 0; i < PPT; ++i)
+        if (kFull || tid + kThreads * i < PIECES) gq[i] = *piece_src(rt_begin, 0, tid + kThreads * i);
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) *piece_dst(0, tid + 256 * i) = gq[i];
+    for (int i = 0; i < PPT; ++i)
+        if (kFull || tid + kThreads * i < PIECES) *piece_dst(0, tid + kThreads * i) = gq[i];
     __syncthreads();
     for (int rt = rt_begin; rt < rt_end; ++rt) {
-        // key tiles of this wave that hold a block complete for the tile's last row
+        // key tiles that hold a block complete for the tile's last row
         const int64_t last = ((int64_t)rt * 32 + 31) < a.rows ? ((int64_t)rt * 32 + 31) : a.rows - 1;
         const int64_t climit = complete_blocks(a, last);
         int ntl = 0;
 #pragma unroll
         for (int t = 0; t < NKT; ++t)
-            if ((key0 + t * 32) / a.B < climit) ntl = t + 1;
+            if ((key0 + t * 32) / BS < climit) ntl = t + 1;
         for (int s = 0; s < gm.stages; ++s) {
             const bool last_stage = s + 1 == gm.stages;
             const int nrt = last_stage ? rt + 1 : rt;   // the next stage
@@ -224,11 +253,13 @@ __global__ __launch_bounds__(256) void score_rows_kernel(RowScoreArgs a, RowGeom
             const bool more = nrt < rt_end;
             if (more)   // in flight while this stage is multiplied
 #pragma unroll
-                for (int i = 0; i < PPT; ++i) gq[i] = *piece_src(nrt, ns, tid + 256 * i);
+                for (int i = 0; i < PPT; ++i)
+                    if (kFull || tid + kThreads * i < PIECES) gq[i] = *piece_src(nrt, ns, tid + kThreads * i);
             if (ntl > 0) stage_mfma(buf, s, ntl);
             if (more)   // that buffer was last read before the previous barrier
 #pragma unroll
-                for (int i = 0; i < PPT; ++i) *piece_dst(buf ^ 1, tid + 256 * i) = gq[i];
+                for (int i = 0; i < PPT; ++i)
+                    if (kFull || tid + kThreads * i < PIECES) *piece_dst(buf ^ 1, tid + kThreads * i) = gq[i];
             __syncthreads();
             buf ^= 1;
         }
@@ -279,41 +310,59 @@ __global__ __launch_bounds__(256) void fill_tail_cols_kernel(float* scores, int6
     scores[r * stride + n + (i - r * w)] = -__builtin_inff();
 }
 
-// 32-key tiles per wave: the keys take NKT * HK * R / 4 registers, kept at 128
-constexpr int nkt_rows(int r, int hk) {
-    const int t = 32 / (hk * (r / 16));
+// 32-key tiles per wave: the keys take NKT * KPW * R / 4 registers, kept at
+// PRED_ROWS_KEY_REGS
+#ifndef PRED_ROWS_KEY_REGS
+#define PRED_ROWS_KEY_REGS 96
+#endif
+constexpr int nkt_rows(int r, int kpw) {
+    const int t = (PRED_ROWS_KEY_REGS / 4) / (kpw * (r / 16));
     return t < 1 ? 1 : (t > 4 ? 4 : t);
 }
 
-template <int R, int HK>
+template <int R, int KPW, int BS>
 hipError_t launch_rk(const RowScoreArgs& a, hipStream_t st) {
-    constexpr int NKT = nkt_rows(R, HK);
+    constexpr int NKT = nkt_rows(R, KPW);
+    const int qh = a.Hq / kWaves;
+    const int sh = (R <= PRED_ROWS_SH2_MAX_R && qh % 2 == 0) ? 2 : 1;
     RowGeom gm;
-    const int64_t n_keys = a.n * a.B;
-    const int64_t keys_per_group = (int64_t)kWaves * NKT * 32;
-    gm.groups = (n_keys + keys_per_group - 1) / keys_per_group;
+    const int64_t n_keys = a.n * BS;
+    gm.groups = (n_keys + kKG * NKT * 32 - 1) / (kKG * NKT * 32);
     gm.row_tiles = (int)((a.rows + 31) / 32);
-    gm.stages = (a.Hq + kStageHeads - 1) / kStageHeads;
-    int64_t parts = (kTargetWaves + gm.groups * kWaves - 1) / (gm.groups * kWaves);
+    gm.stages = qh / sh;
+    int64_t parts = (kTargetWaves + gm.groups * kWaves * kKG - 1) / (gm.groups * kWaves * kKG);
     if (parts > gm.row_tiles) parts = gm.row_tiles;
     if (parts < 1) parts = 1;
     gm.tiles_per_part = (int)((gm.row_tiles + parts - 1) / parts);
     gm.parts = (gm.row_tiles + gm.tiles_per_part - 1) / gm.tiles_per_part;   // no empty parts
     const int64_t wgs = gm.groups * gm.parts;
     if (!grid_fits(wgs)) return hipErrorInvalidConfiguration;
-    score_rows_kernel<R, HK, NKT><<<(unsigned)wgs, 256, 0, st>>>(a, gm);
+    if constexpr (R <= PRED_ROWS_SH2_MAX_R) {
+        if (sh == 2) {
+            score_rows_kernel<R, KPW, NKT, 2, BS><<<(unsigned)wgs, kThreads, 0, st>>>(a, gm);
+            return hipGetLastError();
+        }
+    }
+    score_rows_kernel<R, KPW, NKT, 1, BS><<<(unsigned)wgs, kThreads, 0, st>>>(a, gm);
     return hipGetLastError();
 }
 
-template <int HK>
-hipError_t launch_hk(const RowScoreArgs& a, hipStream_t st) {
+template <int R, int KPW>
+hipError_t launch_rb(const RowScoreArgs& a, hipStream_t st) {
+    switch (a.B) {
+        case 8: return launch_rk<R, KPW, 8>(a, st);
+        case 16: return launch_rk<R, KPW, 16>(a, st);
+        default: return launch_rk<R, KPW, 32>(a, st);
+    }
+}
+
+template <int KPW>
+hipError_t launch_kpw(const RowScoreArgs& a, hipStream_t st) {
     switch (a.R) {
-        case 16: return launch_rk<16, HK>(a, st);
-        case 32: return launch_rk<32, HK>(a, st);
-        case 64: return launch_rk<64, HK>(a, st);
-        default:
-            if constexpr (HK <= 4) return launch_rk<128, HK>(a, st);
-            return hipErrorInvalidValue;   // excluded by rows_mfma_supported
+        case 16: return launch_rb<16, KPW>(a, st);
+        case 32: return launch_rb<32, KPW>(a, st);
+        case 64: return launch_rb<64, KPW>(a, st);
+        default: return launch_rb<128, KPW>(a, st);
     }
 }
 
@@ -321,7 +370,7 @@ bool rows_mfma_supported(const RowScoreArgs& a) {
     const bool r_ok = a.R == 16 || a.R == 32 || a.R == 64 || a.R == 128;
     const bool hk_ok = a.Hk == 1 || a.Hk == 2 || a.Hk == 4 || a.Hk == 8;
     const bool b_ok = a.B == 8 || a.B == 16 || a.B == 32;
-    return r_ok && hk_ok && b_ok && a.Hk * a.R <= 512;
+    return r_ok && hk_ok && b_ok && a.Hq % kWaves == 0;
 }
 
 }  // namespace
@@ -340,13 +389,7 @@ hipError_t launch_score_rows(const RowScoreArgs& a, hipStream_t st) {
     m.n = n_cols;
     const int64_t tail = a.rows * (a.stride - n_cols);
     if (!grid_fits((tail + 255) / 256)) return hipErrorInvalidConfiguration;
-    hipError_t e;
-    switch (a.Hk) {
-        case 1: e = launch_hk<1>(m, st); break;
-        case 2: e = launch_hk<2>(m, st); break;
-        case 4: e = launch_hk<4>(m, st); break;
-        default: e = launch_hk<8>(m, st); break;
-    }
+    const hipError_t e = a.Hk == 8 ? launch_kpw<2>(m, st) : launch_kpw<1>(m, st);
     if (e != hipSuccess || tail == 0) return e;
     fill_tail_cols_kernel<<<(unsigned)((tail + 255) / 256), 256, 0, st>>>(a.scores, a.rows, a.stride, n_cols);
     return hipGetLastError();
