@@ -1,8 +1,8 @@
 """Throughput of the block predictor's hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of the workload:
-project_kv_block (the step's new blocks), project_q, score_blocks and
-rank_victims (see rank_kv_block_amd/workloads.py).  The default workload is the
+project_kv_block (the step's new blocks) and project_q (one pred_project_step
+call), score_blocks and rank_victims (see rank_kv_block_amd/workloads.py).  The default workload is the
 Llama-3-8B-shaped decode step: 32 layers x 8192 blocks, 2 GiB of A_g per step.
 
 Prints one JSON line.  `value` is the A_g bytes the step's scoring reads per
@@ -146,8 +146,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         l0 = wl.layer0_for_step(i)
-        rk.pred_project_kv_block(wl.h, l0, wl.k_new[l0:l0 + nl], wl.table_new[l0:l0 + nl])
-        rk.pred_project_q(wl.h, wl.q[l0:l0 + nl], wl.q_proj)
+        rk.pred_project_step(wl.h, l0, wl.k_new[l0:l0 + nl], wl.table_new[l0:l0 + nl], wl.q[l0:l0 + nl], wl.q_proj)
         ev[i][0].record(stream)
         rk.pred_score_blocks(wl.h, l0, wl.q_proj, wl.tables, wl.scores)
         ev[i][1].record(stream)
@@ -162,7 +161,7 @@ def main():
 
     # per-call breakdown of a step, in a separate loop so the timed steps above
     # carry no extra events: median of 20 steps per entry point
-    names = ["project_kv_block", "project_q", "score_blocks", "rank_victims", "score_blocks_masked"]
+    names = ["project_kv_block", "project_q", "project_step", "score_blocks", "rank_victims", "score_blocks_masked"]
     evs = {k: [] for k in names}
     # the decode case of a partly filled last block: half of block_size + 1 tokens in every sequence
     fill = torch.full((c.S,), c.B // 2 + 1, dtype=torch.int32, device="cuda")
@@ -171,6 +170,8 @@ def main():
         calls = [
             lambda: rk.pred_project_kv_block(wl.h, l0, wl.k_new[l0:l0 + nl], wl.table_new[l0:l0 + nl]),
             lambda: rk.pred_project_q(wl.h, wl.q[l0:l0 + nl], wl.q_proj),
+            lambda: rk.pred_project_step(wl.h, l0, wl.k_new[l0:l0 + nl], wl.table_new[l0:l0 + nl], wl.q[l0:l0 + nl],
+                                         wl.q_proj),
             lambda: rk.pred_score_blocks(wl.h, l0, wl.q_proj, wl.tables, wl.scores),
             lambda: rk.pred_rank_victims(wl.h, wl.scores.view(nl * c.S, c.n), wl.victims, wl.workspace),
             lambda: rk.pred_score_blocks_masked(wl.h, l0, wl.q_proj, wl.tables, fill, wl.scores),

@@ -129,6 +129,23 @@ int pred_project_q(pred_t* p, const pred_bf16* q, int64_t n_vec, pred_bf16* q_pr
 int pred_project_kv_block(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* k,
                           const int32_t* block_table, int64_t n_blocks, void* stream);
 
+/* The two projections of one decode step in one call: exactly
+ * pred_project_kv_block(p, layer0, n_layers, k_new, new_table, n_new, stream)
+ * followed by pred_project_q(p, q, n_vec, q_proj, stream), with the same
+ * arguments, checks and results (predictor.rs page: project_kv_block and
+ * project_q, both run once per step).  Both parts are checked before either is
+ * enqueued.  When both are small (a decode step's one new block per layer and
+ * its query rows) they share one kernel launch, which saves a launch's fixed
+ * cost on the step's critical path; larger calls take the two usual launches.
+ *   k_new      device, [n_layers, n_new, block_size, num_kv_heads, head_dim] bf16
+ *   new_table  device, [n_layers, n_new] int32 or NULL (slots 0..n_new-1)
+ *   q          device, [n_vec, num_q_heads, head_dim] bf16
+ *   q_proj     device, [n_vec, num_q_heads, r] bf16 output
+ * A zero count skips its part. */
+int pred_project_step(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* k_new,
+                      const int32_t* new_table, int64_t n_new, const pred_bf16* q, int64_t n_vec,
+                      pred_bf16* q_proj, void* stream);
+
 /* Block scores (predictor.rs page, score_blocks, extended to several layers,
  * sequences and query rows).
  *   q_proj        device, [n_layers, n_seqs, n_rows, num_q_heads, r] bf16
@@ -229,8 +246,8 @@ int pred_select_keep(pred_t* p, const float* scores, int64_t rows, int64_t strid
 
 /* One decode step in one call: the step's new blocks into A_g, q_proj of every
  * layer, block scores and each (layer, sequence) row's k lowest blocks in
- * eviction order -- pred_project_kv_block, pred_project_q,
- * pred_score_blocks_masked and pred_select_victims (pred_rank_victims when
+ * eviction order -- pred_project_step (pred_project_kv_block and
+ * pred_project_q), pred_score_blocks_masked and pred_select_victims (pred_rank_victims when
  * k = n_blocks) on one stream, in that order, with the same arguments and
  * results (predictor.rs page: project_q, project_kv_block and score_blocks of
  * one step; module doc: the scores rank eviction victims).

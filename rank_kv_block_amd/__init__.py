@@ -149,6 +149,28 @@ def pred_project_kv_block(h, layer0, k, block_table=None, stream=None):
                                        _stream(stream)))
 
 
+def pred_project_step(h, layer0, k_new, new_table, q, q_proj, stream=None):
+    """pred_project_kv_block(h, layer0, k_new, new_table) then pred_project_q(h, q, q_proj), in one call:
+    k_new [n_layers, n_new, B, Hk, D] bf16 (new_table [n_layers, n_new] int32 or None); q [n_vec, Hq, D]
+    -> q_proj [n_vec, Hq, R] (any leading shape, flattened)."""
+    import torch
+    d = pred_get_dims(h)
+    bt = _bf16_types()
+    if k_new.dim() != 5 or tuple(k_new.shape[2:]) != (d.block_size, d.num_kv_heads, d.head_dim):
+        raise ValueError(f"k_new must be [n_layers, n_new, {d.block_size}, {d.num_kv_heads}, {d.head_dim}]")
+    n_layers, n_new = k_new.shape[0], k_new.shape[1]
+    if new_table is not None and tuple(new_table.shape) != (n_layers, n_new):
+        raise ValueError("new_table must be [n_layers, n_new]")
+    if q.numel() % (d.num_q_heads * d.head_dim):
+        raise ValueError("q size does not match [*, num_q_heads, head_dim]")
+    n_vec = q.numel() // (d.num_q_heads * d.head_dim)
+    if q_proj.numel() != n_vec * d.num_q_heads * d.r:
+        raise ValueError("q_proj has the wrong number of elements")
+    _check(lib().pred_project_step(h, layer0, n_layers, _ptr(k_new, "k_new", bt),
+                                   _ptr(new_table, "new_table", (torch.int32,)), n_new, _ptr(q, "q", bt), n_vec,
+                                   _ptr(q_proj, "q_proj", bt), _stream(stream)))
+
+
 def pred_score_blocks(h, layer0, q_proj, block_tables, scores, stream=None):
     """q_proj [n_layers, n_seqs, n_rows, Hq, R]; block_tables [n_seqs, n_blocks] int32 or None;
     scores [n_layers, n_seqs, n_blocks] float32."""

@@ -61,6 +61,7 @@ SIGNATURES = {
     "pred_destroy": (None, [_vp]),
     "pred_project_q": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp]),
     "pred_project_kv_block": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _i64, _vp]),
+    "pred_project_step": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _i64, _vp, _i64, _vp, _vp]),
     "pred_score_blocks": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _i64, _i32, _vp, _vp]),
     "pred_score_blocks_masked": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _i64, _i32, _vp, _vp, _vp]),
     "pred_rank_victims": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp]),

@@ -21,6 +21,11 @@ hipError_t launch_project_dense(const uint16_t* in, const double* pf, uint16_t* 
 hipError_t launch_project_paged(const uint16_t* k, const double* pf, uint16_t* a_first,
                                 const int32_t* table, int n_layers, int64_t n_blocks, int64_t N, int Hk,
                                 int B, int D, int R, uint32_t* err, hipStream_t stream);
+// Both of the above, in that order and with the same results; one launch when
+// both are small (a decode step), otherwise the two launches.
+hipError_t launch_project_pair(const uint16_t* k, uint16_t* a_first, const int32_t* table, int n_layers,
+                               int64_t n_blocks, int64_t N, int Hk, int B, uint32_t* err, const uint16_t* q,
+                               uint16_t* q_out, int64_t n_q, const double* pf, int D, int R, hipStream_t stream);
 
 // ---- scores (score_decode.hip, score_prefill.hip) --------------------------
 struct ScoreArgs {

@@ -259,6 +259,25 @@ int project_kv_impl(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16
     return ok();
 }
 
+// project_kv_block then project_q, both checked before either is enqueued; the
+// two small projections of a decode step share one launch.
+int project_step_impl(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* k, const int32_t* new_table,
+                      int64_t n_new, const pred_bf16* q, int64_t n_vec, pred_bf16* q_proj, void* stream, bool go) {
+    int rc = project_kv_impl(p, layer0, n_layers, k, new_table, n_new, stream, false);
+    if (rc == 0) rc = project_q_impl(p, q, n_vec, q_proj, stream, false);
+    if (rc || !go) return rc;
+    const pred_dims& d = p->d;
+    const bool kv_work = n_new > 0 && n_layers > 0;
+    const int64_t rows = n_vec > 0 ? n_vec * d.num_q_heads : 0;   // product checked by project_q_impl
+    uint16_t* a_first = p->ag_dev + (int64_t)layer0 * d.max_blocks * d.num_kv_heads * d.block_size * d.r;
+    hipError_t e = pred::launch_project_pair(kv_work ? k : nullptr, a_first, new_table, kv_work ? n_layers : 0,
+                                             kv_work ? n_new : 0, d.max_blocks, d.num_kv_heads, d.block_size,
+                                             p->err_dev, q, q_proj, rows, p->pf_dev, d.head_dim, d.r,
+                                             (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "project_step launch");
+    return ok();
+}
+
 int score_impl(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* q_proj, int32_t n_rows,
                const int32_t* block_tables, int64_t n_blocks, int32_t n_seqs, const int32_t* last_fill,
                float* scores, void* stream, bool go) {
@@ -311,6 +330,11 @@ int pred_project_q(pred_t* p, const pred_bf16* q, int64_t n_vec, pred_bf16* q_pr
 int pred_project_kv_block(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* k,
                           const int32_t* block_table, int64_t n_blocks, void* stream) {
     return project_kv_impl(p, layer0, n_layers, k, block_table, n_blocks, stream, true);
+}
+
+int pred_project_step(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* k_new, const int32_t* new_table,
+                      int64_t n_new, const pred_bf16* q, int64_t n_vec, pred_bf16* q_proj, void* stream) {
+    return project_step_impl(p, layer0, n_layers, k_new, new_table, n_new, q, n_vec, q_proj, stream, true);
 }
 
 int pred_score_blocks(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* q_proj, int32_t n_rows,
@@ -430,8 +454,7 @@ int pred_decode_step(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf1
     // every part is checked before anything is enqueued
     for (int pass = 0; pass < 2; ++pass) {
         const bool go = pass == 1;
-        int rc = project_kv_impl(p, layer0, n_layers, k_new, new_table, n_new, stream, go);
-        if (rc == 0) rc = project_q_impl(p, q, n_vec, q_proj, stream, go);
+        int rc = project_step_impl(p, layer0, n_layers, k_new, new_table, n_new, q, n_vec, q_proj, stream, go);
         if (rc == 0)
             rc = score_impl(p, layer0, n_layers, q_proj, n_rows, block_tables, n_blocks, n_seqs, last_fill, scores,
                             stream, go);

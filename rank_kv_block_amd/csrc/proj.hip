@@ -219,16 +219,12 @@ __device__ inline void load_words(const uint16_t* p, uint32_t (&wd)[DW / 2]) {
 
 // One workgroup per (16-vector tile, 16-column tile); wave w sums head_dim
 // values [w*D/4, (w+1)*D/4), lane group q the DW of them starting at
-// w*D/4 + q*DW (DW = D/16 k-steps per wave).
+// w*D/4 + q*DW (DW = D/16 k-steps per wave).  `unit` is the workgroup's tile.
 template <int DW>
-__global__ __launch_bounds__(256) void project_splitk_kernel(const uint16_t* __restrict__ in,
-                                                             const double* __restrict__ pf, OutMap om,
-                                                             int64_t n_vec, int64_t units) {
-    __shared__ f64x4_t part[3][64];
+__device__ inline void splitk_unit(const uint16_t* __restrict__ in, const double* __restrict__ pf, const OutMap& om,
+                                   int64_t n_vec, int64_t unit, f64x4_t (*part)[64]) {
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const int64_t unit = blockIdx.x;
-    if (unit >= units) return;   // whole workgroup
     const int D = 16 * DW;
     const int R = om.R;
     const int jtiles = R >> 4;
@@ -276,6 +272,30 @@ __global__ __launch_bounds__(256) void project_splitk_kernel(const uint16_t* __r
         if (off[v] >= 0) om.out[off[v] + j] = f64_to_bf16_rne(acc[v]);
         else if (off[v] == -1 && col == 0 && jt == 0) atomicOr(om.err, DEVERR_TABLE);
     }
+}
+
+template <int DW>
+__global__ __launch_bounds__(256) void project_splitk_kernel(const uint16_t* __restrict__ in,
+                                                             const double* __restrict__ pf, OutMap om,
+                                                             int64_t n_vec, int64_t units) {
+    __shared__ f64x4_t part[3][64];
+    if ((int64_t)blockIdx.x >= units) return;   // whole workgroup
+    splitk_unit<DW>(in, pf, om, n_vec, blockIdx.x, part);
+}
+
+// Two small projections in one launch (a decode step's new KV blocks and its
+// queries): workgroups [0, units0) take the first job's tiles, the rest the
+// second's.  Each tile is computed exactly as by project_splitk_kernel.
+template <int DW>
+__global__ __launch_bounds__(256) void project_splitk_pair_kernel(const uint16_t* __restrict__ in0, OutMap om0,
+                                                                  int64_t n0, int64_t units0,
+                                                                  const uint16_t* __restrict__ in1, OutMap om1,
+                                                                  int64_t n1, int64_t units1,
+                                                                  const double* __restrict__ pf) {
+    __shared__ f64x4_t part[3][64];
+    const int64_t u = blockIdx.x;
+    if (u < units0) splitk_unit<DW>(in0, pf, om0, n0, u, part);
+    else if (u - units0 < units1) splitk_unit<DW>(in1, pf, om1, n1, u - units0, part);
 }
 
 bool mfma_path(int D, int R) { return (D == 32 || D == 64 || D == 128 || D == 256) && R % 16 == 0; }
@@ -365,6 +385,35 @@ hipError_t launch_project_paged(const uint16_t* k, const double* pf, uint16_t* a
     }
 #undef PRED_PAGED
     return hipGetLastError();
+}
+
+hipError_t launch_project_pair(const uint16_t* k, uint16_t* a_first, const int32_t* table, int n_layers,
+                               int64_t n_blocks, int64_t N, int Hk, int B, uint32_t* err, const uint16_t* q,
+                               uint16_t* q_out, int64_t n_q, const double* pf, int D, int R, hipStream_t stream) {
+    const int64_t n_k = (int64_t)n_layers * n_blocks * B * Hk;
+    const int jtiles = R / 16;
+    const int64_t units_k = (n_k + 15) / 16 * jtiles;
+    const int64_t units_q = (n_q + 15) / 16 * jtiles;
+    // one launch only where each job on its own would take the split-head_dim kernel
+    if (n_k > 0 && n_q > 0 && mfma_path(D, R) && units_k < PRED_PROJ_SPLITK_BELOW &&
+        units_q < PRED_PROJ_SPLITK_BELOW) {
+        const OutMap om_k{a_first, table, err, n_blocks, N, Hk, B, R, true};
+        const OutMap om_q{q_out, nullptr, nullptr, 0, 0, 0, 0, R, false};
+        const unsigned grid = (unsigned)(units_k + units_q);
+#define PRED_PAIR(DWV)                                                                                       \
+    project_splitk_pair_kernel<DWV><<<grid, 256, 0, stream>>>(k, om_k, n_k, units_k, q, om_q, n_q, units_q, pf)
+        switch (D) {
+            case 32: PRED_PAIR(2); break;
+            case 64: PRED_PAIR(4); break;
+            case 128: PRED_PAIR(8); break;
+            default: PRED_PAIR(16); break;
+        }
+#undef PRED_PAIR
+        return hipGetLastError();
+    }
+    hipError_t e = launch_project_paged(k, pf, a_first, table, n_layers, n_blocks, N, Hk, B, D, R, err, stream);
+    if (e != hipSuccess) return e;
+    return launch_project_dense(q, pf, q_out, n_q, D, R, stream);
 }
 
 }  // namespace pred

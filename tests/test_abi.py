@@ -95,6 +95,7 @@ def test_null_handle_errors():
     assert "NULL" in rk.pred_last_error()
     assert lib.pred_project_kv_block(None, 0, 1, None, None, 1, None) == rk.PRED_ERR_NULL_ARG
     assert lib.pred_score_blocks(None, 0, 1, None, 1, None, 1, 1, None, None) == rk.PRED_ERR_NULL_ARG
+    assert lib.pred_project_step(None, 0, 1, None, None, 1, None, 1, None, None) == rk.PRED_ERR_NULL_ARG
     assert lib.pred_rank_victims(None, None, 1, 1, None, None, 0, None) == rk.PRED_ERR_NULL_ARG
     assert lib.pred_device_error(None, None) == rk.PRED_ERR_NULL_ARG
     assert lib.pred_a_g_ptr(None) is None
