@@ -69,6 +69,7 @@ __device__ inline uint32_t order_key(float x) {
 // MFMA operand and accumulator types (v_mfma_f32_32x32x16_bf16).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // 16 bytes as a plain vector (uint4 is a union-based struct, which keeps arrays
 // of it from being split into registers)
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));

@@ -329,6 +329,165 @@ void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
     }
 }
 
+// Matrix-core variant for kv heads with 5..16 queries (rows x GQA group), where
+// the dot products above would cost ~8-16 VALU instructions per loaded word.
+// It streams A_g exactly as the kernel above (one contiguous 1 KiB wave-load per
+// load slot, slot offsets in SGPRs) and multiplies each wave-load on
+// v_mfma_f32_16x16x32_bf16 against the kv head's queries (B operand [32, 16]:
+// column n is query n, columns past the query count repeat a real query).
+//
+// A wave-load holds 16 / H token rows of R values, H = R / 32.  The MFMA's 16
+// A rows are (token, part) pairs: row m is part m % H (values [32p, 32p + 32))
+// of token m / H, and lane (m, c) = (lane % 16, lane / 16) takes 16-byte piece
+// 4p + c of that row -- a permutation of the 1 KiB, so the load stays one
+// contiguous access.  MFMA j multiplies the whole tile by values
+// [32j, 32j + 32) of the queries; row m is meaningful in MFMA j = m % H only,
+// and the full dot product of a token is the sum over its H rows, each from its
+// own MFMA.  Accumulator lane (n, c) holds rows 4c .. 4c + 3 of column n, i.e.
+// tokens 4c/H .. of the wave-load, so the sums stay inside a lane: token
+// 4c/H + v gets sum over p of C_p[v*H + p].
+template <int R, int NS>
+__global__ __launch_bounds__(256) void score_decode_mfma_kernel(ScoreArgs a, DecodeGeom gm) {
+    constexpr int H = R / 32;             // parts per token row = MFMAs per wave-load
+    constexpr int ROWB = R * 2;           // bytes per token row
+    constexpr int TPL = 4 / H;            // tokens per accumulator lane per wave-load
+    static_assert(NS <= 16, "4 live bits per load slot in 64 bits");
+    extern __shared__ uint4 q_lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t wgb = blockIdx.x % gm.wgs_per_seq;
+    const int64_t ls = blockIdx.x / gm.wgs_per_seq;
+    const int s = (int)(ls % a.S);
+    const int l = (int)(ls / a.S);
+    const int64_t b_first = (wgb * kWaves + wave_id) * gm.NBW;
+    const uint16_t* qrows = a.qp + ((int64_t)l * a.S + s) * (int64_t)a.M * a.Hq * R;
+    const bool has_work = b_first < a.n;
+    const int m = lane & 15;
+    const int c = lane >> 4;
+    const int g = a.Hq / a.Hk;
+    const int64_t layer = a.layer0 + l;
+    const int64_t slot_bytes = (int64_t)a.Hk * a.B * ROWB;
+    const char* slab = reinterpret_cast<const char*>(a.ag + layer * a.N * (slot_bytes >> 1));
+    int32_t tab_lane = -1;
+    {
+        const int64_t b = b_first + lane;
+        if (lane < gm.NBW && b < a.n) tab_lane = a.tables ? a.tables[(int64_t)s * a.n + b] : (int32_t)b;
+    }
+    const int fill_s = fill_of(a, s);
+    if (a.fill && wgb == 0 && threadIdx.x == 0 && (a.fill[s] < 0 || a.fill[s] > a.B)) atomicOr(a.err, DEVERR_FILL);
+    // Slot sl: block bi = sl / SPB, wave-load sl % SPB of its kv region (tokens
+    // (sl % SPB) * 16 / H ..).  live: TPL bits per slot, token 4c/H + v scored.
+    uint32_t soff_slot[NS];
+    uint64_t live = 0;
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+        const int bi = (sl * 64) >> gm.log2U;
+        const int piece = sl - bi * gm.SPB;
+        const int32_t phys = __builtin_amdgcn_readlane(tab_lane, bi);
+        const bool ok = bi < gm.NBW && b_first + bi < a.n && phys >= 0 && (int64_t)phys < a.N;
+        soff_slot[sl] = (uint32_t)((ok ? (int64_t)phys : 0) * slot_bytes + 1024 * piece);
+        const bool last = b_first + bi == a.n - 1;
+        uint32_t bits = 0;
+#pragma unroll
+        for (int v = 0; v < TPL; ++v) {
+            const int tok = piece * (16 / H) + (4 * c) / H + v;
+            bits |= ((ok && !(last && tok >= fill_s)) ? 1u : 0u) << v;
+        }
+        live |= (uint64_t)bits << (4 * sl);
+    }
+    float rm[NS];
+#pragma unroll
+    for (int t = 0; t < NS; ++t) rm[t] = -__builtin_inff();
+
+    // query column m of kv head 0, 16-byte units; the kv head adds g*R/8, MFMA j adds 4j
+    const int e = m < gm.n_eff ? m : gm.n_eff - 1;
+    const int qrow = e / g;
+    const int qoff = (int)((((int64_t)qrow * a.Hq + (e - qrow * g)) * R + c * 8) >> 3);
+    const int q_kv_step = g * R / 8;
+    const int64_t kv_bytes = (int64_t)a.B * ROWB;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(slab), (short)0, (int)0xFFFFFFFF, 0x00020000);
+    const int voff = (m / H) * ROWB + ((m % H) * 4 + c) * 16;
+    auto load_a = [&](u32x4_t (&dst)[NS], int kv) {
+        const uint32_t kvoff = (uint32_t)(kv * kv_bytes);
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl)
+            dst[sl] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rsrc, voff, (int)(soff_slot[sl] + kvoff), PRED_DECODE_AUX));
+    };
+    auto score_kv = [&](const u32x4_t (&av)[NS], int kv) {
+        bf16x8_t qb[H];
+#pragma unroll
+        for (int j = 0; j < H; ++j) qb[j] = __builtin_bit_cast(bf16x8_t, q_lds[qoff + kv * q_kv_step + j * 4]);
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+            f32x4_t cp[H];
+#pragma unroll
+            for (int j = 0; j < H; ++j)
+                cp[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[sl]), qb[j],
+                                                                f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            const uint32_t bits = (uint32_t)(live >> (4 * sl)) & 0xFu;
+            float mx = rm[sl];
+#pragma unroll
+            for (int v = 0; v < TPL; ++v) {
+                float d = cp[0][v * H];
+#pragma unroll
+                for (int j = 1; j < H; ++j) d += cp[j][v * H + j];
+                mx = ((bits >> v) & 1u) ? fmaxf(mx, d) : mx;
+            }
+            rm[sl] = mx;
+        }
+    };
+
+    const int kv0 = PRED_DECODE_ROTATE ? (int)((b_first / gm.NBW) % a.Hk) : 0;
+    auto kvr = [&](int k) { const int r = kv0 + k; return r < a.Hk ? r : r - a.Hk; };
+    u32x4_t A0[NS], A1[NS];
+    if (has_work) load_a(A0, kvr(0));
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(qrows);
+        for (int i = threadIdx.x; i < gm.q_chunks; i += 256) q_lds[i] = src[i];
+        __syncthreads();
+    }
+    if (!has_work) return;   // after the only barrier
+    int kv = 0;
+    for (; kv + 2 < a.Hk; kv += 2) {
+        load_a(A1, kvr(kv + 1));
+        score_kv(A0, kvr(kv));
+        load_a(A0, kvr(kv + 2));
+        score_kv(A1, kvr(kv + 1));
+    }
+    if (kv + 1 < a.Hk) {
+        load_a(A1, kvr(kv + 1));
+        score_kv(A0, kvr(kv));
+        score_kv(A1, kvr(kv + 1));
+    } else {
+        score_kv(A0, kvr(kv));
+    }
+
+    float* out = a.scores + ((int64_t)l * a.S + s) * a.n;
+    const int32_t* table = a.tables ? a.tables + (int64_t)s * a.n : nullptr;
+    float acc = -__builtin_inff();
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+        acc = fmaxf(acc, rm[sl]);
+        if ((sl + 1) % gm.SPB == 0) {
+            const float v = wave_max_xor(acc, 64);
+            const int bi = sl / gm.SPB;
+            const int64_t b = b_first + bi;
+            if (lane == 0 && bi < gm.NBW && b < a.n) {
+                const int64_t phys = table ? (int64_t)table[b] : b;
+                if (phys >= 0 && phys < a.N) {
+                    out[b] = v;
+                } else {
+                    out[b] = __uint_as_float(0x7FC00000u);
+                    atomicOr(a.err, DEVERR_TABLE);
+                }
+            }
+            acc = -__builtin_inff();
+        }
+    }
+}
+
 // Any shape: one thread per (layer, sequence, block), plain loops.  Used when
 // R or block_size is not one the streaming kernel is laid out for.
 __global__ __launch_bounds__(256) void score_generic_kernel(ScoreArgs a) {
@@ -440,6 +599,15 @@ bool decode_geometry(const ScoreArgs& a, DecodeGeom& gm, int& ns, int& lpr, int&
     return true;
 }
 
+// The matrix-core scorer takes kv heads with more than 4 queries (at 4 or fewer
+// the dot products cost ~1% of the stream), r a multiple of 32 up to 128, kv
+// regions of whole wave-loads, 32-bit slab offsets and the query slab in LDS.
+bool decode_mfma_ok(const ScoreArgs& a, const DecodeGeom& gm) {
+    const bool narrow = a.N * (int64_t)a.Hk * a.B * a.R * 2 < (int64_t(1) << 32);
+    return (a.R == 32 || a.R == 64 || a.R == 128) && gm.U >= 64 && narrow &&
+           gm.q_chunks * 16 <= kQLdsMaxBytes && gm.n_eff > 4 && gm.n_eff <= 16;
+}
+
 }  // namespace
 
 hipError_t launch_score_decode_or_generic(const ScoreArgs& a, hipStream_t stream) {
@@ -447,6 +615,22 @@ hipError_t launch_score_decode_or_generic(const ScoreArgs& a, hipStream_t stream
     int ns, lpr, qh;
     if (decode_geometry(a, gm, ns, lpr, qh)) {
         if (!grid_fits(gm.wgs_per_seq * a.S * a.n_layers)) return hipErrorInvalidConfiguration;
+        if (decode_mfma_ok(a, gm)) {
+            const unsigned grid = (unsigned)(gm.wgs_per_seq * a.S * a.n_layers);
+            const int q_bytes = gm.q_chunks * 16;
+#define PRED_DMFMA(RV, NSV) score_decode_mfma_kernel<RV, NSV><<<grid, 256, q_bytes, stream>>>(a, gm)
+            if (ns == 16) {
+                if (a.R == 32) PRED_DMFMA(32, 16);
+                else if (a.R == 64) PRED_DMFMA(64, 16);
+                else PRED_DMFMA(128, 16);
+            } else {
+                if (a.R == 32) PRED_DMFMA(32, 4);
+                else if (a.R == 64) PRED_DMFMA(64, 4);
+                else PRED_DMFMA(128, 4);
+            }
+#undef PRED_DMFMA
+            return hipGetLastError();
+        }
         if (ns == 16) launch_decode_ns<16>(a, gm, lpr, qh, stream);
         else if (ns == 4) launch_decode_ns<4>(a, gm, lpr, qh, stream);
         else launch_decode_ns<8>(a, gm, lpr, qh, stream);
@@ -461,7 +645,8 @@ hipError_t launch_score_decode_or_generic(const ScoreArgs& a, hipStream_t stream
 const char* score_decode_path_name(const ScoreArgs& a) {
     DecodeGeom gm;
     int ns, lpr, qh;
-    return decode_geometry(a, gm, ns, lpr, qh) ? "decode_stream" : "generic";
+    if (!decode_geometry(a, gm, ns, lpr, qh)) return "generic";
+    return decode_mfma_ok(a, gm) ? "decode_mfma" : "decode_stream";
 }
 
 }  // namespace pred

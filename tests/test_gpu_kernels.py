@@ -139,6 +139,14 @@ SHAPES = [
     (1, 12, 4, 64, 24, 16, 30, 30, 1, 1, "perm"),          # r = 24: plain per-block kernel
     (1, 8, 2, 32, 16, 12, 60, 29, 2, 1, "identity"),       # block_size 12: plain per-block kernel
     (1, 16, 2, 64, 128, 32, 40, 37, 1, 1, "perm"),         # 1 KiB-wide kv regions: 16 load slots per wave
+    # 5..16 queries per kv head: the decode scorer's matrix-core variant
+    (2, 16, 2, 64, 32, 16, 100, 45, 2, 1, "perm"),         # r = 32: one 16-token tile, four blocks per wave
+    (1, 16, 1, 64, 64, 64, 30, 19, 1, 1, "perm"),          # block_size 64: four tiles, 16 load slots
+    (1, 16, 2, 128, 128, 16, 40, 21, 1, 2, "identity"),    # r = 128: four k-steps; 2 rows x g = 8 = 16 queries
+    (1, 24, 4, 64, 64, 32, 80, 33, 2, 1, "perm"),          # g = 6: columns 6..15 repeat a query
+    (1, 8, 8, 64, 32, 32, 40, 27, 1, 5, "perm"),           # g = 1, 5 rows
+    (1, 16, 2, 64, 16, 16, 70, 31, 2, 1, "perm"),          # 8 queries at r = 16: vector-ALU decode kernel
+    (1, 8, 1, 64, 32, 8, 40, 23, 1, 1, "perm"),            # 8 queries, 512-byte kv regions: vector-ALU kernel
     (2, 32, 8, 128, 32, 16, 9000, 8200, 1, 1, "perm"),     # larger ragged case, two layers
     (1, 8, 2, 256, 32, 16, 40, 21, 1, 1, "identity"),      # head_dim 256: widest MFMA projection tiles
     (1, 8, 2, 96, 16, 16, 40, 20, 2, 1, "perm"),           # head_dim 96: plain projection kernel

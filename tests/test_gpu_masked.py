@@ -35,6 +35,8 @@ MASK_SHAPES = [
     (32, 8, 64, 32, 16, 200, 60, 3, 1, 2),     # decode stream, one wave-load per kv region
     (8, 2, 64, 16, 8, 100, 45, 2, 1, 1),       # decode stream, several blocks per wave-load
     (8, 1, 64, 128, 32, 40, 13, 2, 1, 1),      # decode stream, 16 load slots
+    (64, 8, 64, 64, 32, 160, 21, 7, 1, 1),     # decode matrix-core variant: 8 queries, two tiles per block
+    (16, 2, 64, 32, 16, 160, 22, 7, 1, 1),     # decode matrix-core variant: four blocks per wave
     (32, 8, 64, 64, 16, 80, 37, 2, 8, 1),      # many-row MFMA scorer
     (4, 2, 32, 24, 16, 40, 19, 2, 1, 1),       # plain kernel
 ]
