@@ -295,20 +295,21 @@ def main():
     blocks = c.blocks_per_step
     a_g_bytes = blocks * c.slot_bytes
     aux_bytes = blocks * 8 + nl * c.S * c.M * c.Hq * c.R * 2      # table entry + score per block, q_proj
-    many_row = c.M * c.g > 16
+    kernel = rk.pred_score_kernel_name(wl.h, c.M)
+    many_row = kernel == "score_prefill_kernel"
     if many_row:
         # a contraction: every (query row, head) against every key of every block
         flops = 2.0 * nl * c.S * c.M * c.Hq * c.R * c.n * c.B
         achieved = flops / (score_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS,
                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
-                    "kernel": "score_prefill_kernel", "algorithmic_flops_per_launch": flops,
+                    "kernel": kernel, "algorithmic_flops_per_launch": flops,
                     "algorithmic_bytes_per_launch": a_g_bytes + aux_bytes}
     else:
         achieved = a_g_bytes / (score_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic(c.name, a_g_bytes),
-                    "kernel": "score_decode_kernel", "algorithmic_bytes_per_launch": a_g_bytes,
+                    "kernel": kernel, "algorithmic_bytes_per_launch": a_g_bytes,
                     "aux_bytes_per_launch": aux_bytes}
     out = {
         "metric": "score_blocks A_g GB/s (% of HBM peak) and blocks scored/s, 1 GPU",
@@ -331,7 +332,7 @@ def main():
         "score_kernel_ms": round(score_ms, 4),
         "score_kernel_us": {"median": round(score_each[len(score_each) // 2] * 1e3, 2),
                             "min": round(score_each[0] * 1e3, 2), "max": round(score_each[-1] * 1e3, 2)},
-        "score_kernel_path": "many_row" if many_row else "decode_stream",
+        "score_kernel_path": kernel,
         "roofline": roofline,
     }
     out["step_breakdown_median_us"] = breakdown

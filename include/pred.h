@@ -205,6 +205,15 @@ int pred_rank_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t 
 int pred_select_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments, int64_t k,
                         int32_t* victims, void* workspace, size_t ws_bytes, void* stream);
 
+/* Name of the kernel pred_score_blocks (and pred_score_blocks_masked) runs for
+ * this handle's dims and n_rows query rows per sequence (host only, static
+ * string): "score_prefill_kernel" (more than 16 queries per kv head: bf16
+ * MFMA), "score_decode_mfma_kernel" (5 to 16), "score_decode_kernel" (up to 4,
+ * or shapes the matrix-core variant does not take) or "score_generic_kernel"
+ * (r or block_size outside the streaming layouts).  NULL for a NULL handle or
+ * n_rows < 1. */
+const char* pred_score_kernel_name(pred_t* p, int32_t n_rows);
+
 /* Per-row causal block scores of a prefill chunk (qsa_select.rs page, prefill
  * selection: each query row is scored against the blocks complete at its
  * position; the score is the predictor's, predictor.rs page, score_blocks, kept

@@ -303,6 +303,14 @@ def pred_decode_step(h, layer0, k_new, new_table, q, q_proj, block_tables, last_
 
 # ------------------------------------------------------------------ inspection
 
+def pred_score_kernel_name(h, n_rows=1):
+    """The kernel pred_score_blocks runs for this handle with n_rows query rows per sequence."""
+    name = lib().pred_score_kernel_name(h, n_rows)
+    if name is None:
+        raise PredError(PRED_ERR_NULL_ARG if not h else PRED_ERR_OUT_OF_RANGE, pred_last_error())
+    return name.decode()
+
+
 def pred_copy_projection(h):
     d = pred_get_dims(h)
     out = np.empty((d.head_dim, d.r), np.uint16)

@@ -350,6 +350,25 @@ int pred_score_blocks_masked(pred_t* p, int32_t layer0, int32_t n_layers, const 
                       stream, true);
 }
 
+const char* pred_score_kernel_name(pred_t* p, int32_t n_rows) {
+    if (!p || n_rows < 1) {
+        fail(p ? PRED_ERR_OUT_OF_RANGE : PRED_ERR_NULL_ARG, "score_kernel_name: %s", p ? "n_rows < 1" : "NULL handle");
+        return nullptr;
+    }
+    pred::ScoreArgs a{};
+    a.N = p->d.max_blocks;
+    a.n = 1;
+    a.n_layers = 1;
+    a.S = 1;
+    a.M = n_rows;
+    a.Hq = p->d.num_q_heads;
+    a.Hk = p->d.num_kv_heads;
+    a.B = p->d.block_size;
+    a.R = p->d.r;
+    if ((int64_t)a.M * (a.Hq / a.Hk) > 16 && pred::prefill_supported(a)) return "score_prefill_kernel";
+    return pred::score_decode_path_name(a);
+}
+
 int pred_score_rows(pred_t* p, int32_t layer, const pred_bf16* q_proj, int64_t rows, int64_t first_pos,
                     const int32_t* block_table, int64_t n_blocks, float* scores, int64_t stride, void* stream) {
     if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");

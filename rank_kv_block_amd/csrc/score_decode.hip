@@ -38,6 +38,12 @@
 #ifndef PRED_DECODE_WAVES_PER_EU
 #define PRED_DECODE_WAVES_PER_EU 0
 #endif
+// Queries per kv head (rows x GQA group) from which the matrix-core variant
+// scores instead of the vector-ALU dot products (at 4 queries both stream at
+// the same rate: 316 vs 315-318 us for 32 layers x 8192 blocks).
+#ifndef PRED_DECODE_MFMA_MIN_QUERIES
+#define PRED_DECODE_MFMA_MIN_QUERIES 5
+#endif
 
 namespace pred {
 
@@ -605,7 +611,7 @@ bool decode_geometry(const ScoreArgs& a, DecodeGeom& gm, int& ns, int& lpr, int&
 bool decode_mfma_ok(const ScoreArgs& a, const DecodeGeom& gm) {
     const bool narrow = a.N * (int64_t)a.Hk * a.B * a.R * 2 < (int64_t(1) << 32);
     return (a.R == 32 || a.R == 64 || a.R == 128) && gm.U >= 64 && narrow &&
-           gm.q_chunks * 16 <= kQLdsMaxBytes && gm.n_eff > 4 && gm.n_eff <= 16;
+           gm.q_chunks * 16 <= kQLdsMaxBytes && gm.n_eff >= PRED_DECODE_MFMA_MIN_QUERIES && gm.n_eff <= 16;
 }
 
 }  // namespace
@@ -645,8 +651,8 @@ hipError_t launch_score_decode_or_generic(const ScoreArgs& a, hipStream_t stream
 const char* score_decode_path_name(const ScoreArgs& a) {
     DecodeGeom gm;
     int ns, lpr, qh;
-    if (!decode_geometry(a, gm, ns, lpr, qh)) return "generic";
-    return decode_mfma_ok(a, gm) ? "decode_mfma" : "decode_stream";
+    if (!decode_geometry(a, gm, ns, lpr, qh)) return "score_generic_kernel";
+    return decode_mfma_ok(a, gm) ? "score_decode_mfma_kernel" : "score_decode_kernel";
 }
 
 }  // namespace pred

@@ -99,6 +99,7 @@ def test_null_handle_errors():
     assert lib.pred_rank_victims(None, None, 1, 1, None, None, 0, None) == rk.PRED_ERR_NULL_ARG
     assert lib.pred_device_error(None, None) == rk.PRED_ERR_NULL_ARG
     assert lib.pred_a_g_ptr(None) is None
+    assert lib.pred_score_kernel_name(None, 1) is None
     lib.pred_destroy(None)
 
 

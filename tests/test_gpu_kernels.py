@@ -160,6 +160,24 @@ SHAPES = [
 ]
 
 
+def test_parity_shapes_reach_every_score_kernel():
+    """The shapes below exercise each kernel pred_score_blocks can launch."""
+    seen = {}
+    for L, Hq, Hk, D, R, B, N, n, S, M, table in SHAPES:
+        with rk.Predictor(rk.dims(L, Hq, Hk, D, R, B, N), 1) as p:
+            seen.setdefault(rk.pred_score_kernel_name(p.handle, M), []).append((Hq, Hk, R, B, M))
+    assert set(seen) == {"score_prefill_kernel", "score_decode_mfma_kernel", "score_decode_kernel",
+                         "score_generic_kernel"}, seen
+    with rk.Predictor(rk.dims(1, 64, 8, 128, 64, 32, 16), 1) as p:       # 70B-shaped decode
+        assert rk.pred_score_kernel_name(p.handle, 1) == "score_decode_mfma_kernel"
+        assert rk.pred_score_kernel_name(p.handle, 3) == "score_prefill_kernel"
+    with rk.Predictor(rk.dims(1, 32, 8, 128, 32, 16, 16), 1) as p:       # 8B-shaped decode
+        assert rk.pred_score_kernel_name(p.handle, 1) == "score_decode_kernel"
+        assert rk.pred_score_kernel_name(p.handle, 2) == "score_decode_mfma_kernel"
+        with pytest.raises(rk.PredError):
+            rk.pred_score_kernel_name(p.handle, 0)
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"L{s[0]}-q{s[1]}-kv{s[2]}-d{s[3]}-r{s[4]}-b{s[5]}-n{s[7]}"
                                               f"-S{s[8]}-M{s[9]}" for s in SHAPES])
 def test_random_shape_parity(shape):
