@@ -211,6 +211,9 @@ __global__ __launch_bounds__(TPB) void rank_count_merge_kernel(const uint32_t* _
     const int rlen = rlen0 < kl ? rlen0 : kl;               // elements of its own run placed here
     if (piece * TPB >= rlen) return;                         // whole workgroup: nothing to place
     const uint32_t* src = in_keys + seg * n + g0;
+    const int i = piece * TPB + t;                           // this thread's element of its run
+    // its index, requested now so the load overlaps the group load and the searches
+    const uint32_t id = in_idx[seg * n + run0 + (i < rlen ? i : 0)];
     {
         // the group's keys, padded to G full runs with a key above every real one
         // (order keys never exceed that of +inf); clamped indexes keep every load
@@ -229,7 +232,6 @@ __global__ __launch_bounds__(TPB) void rank_count_merge_kernel(const uint32_t* _
     }
     __syncthreads();
 
-    const int i = piece * TPB + t;                           // this thread's element of its run
     const uint32_t x = gk[own * RL + (i < rlen ? i : 0)];
     const bool pad = x == kPadKey;                           // a row's entries past its eligible count
     int pos = i;                                             // the elements of its own run before it
@@ -249,7 +251,6 @@ __global__ __launch_bounds__(TPB) void rank_count_merge_kernel(const uint32_t* _
         pos += r == own ? 0 : ((pad && r < own) ? RL : lo);
     }
     if (i < rlen && pos < glen && pos < klim) {             // pos < glen always holds
-        const uint32_t id = in_idx[seg * n + run0 + i];
         if (g0 == 0 && glen == n) {
             victims[seg * vstride + pos] = (int32_t)id;
         } else {
