@@ -45,7 +45,7 @@ def _step(wl, k, q_proj, scores, victims, fill=None, stream=None):
                         victims, wl.workspace, stream=stream)
 
 
-@pytest.mark.parametrize("n,M", [(150, 1), (2500, 1), (300, 8)])
+@pytest.mark.parametrize("n,M", [(150, 1), (2500, 1), (300, 8), (400, 2)])
 def test_decode_step_equals_separate_calls(n, M):
     _say("decode_step", n, M)
     wl = _workload(n=n, N=max(600, 3 * n), M=M)
