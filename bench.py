@@ -74,13 +74,20 @@ def cpu_baseline(wl, budget_s=12.0):
     done = 0
     blocks = 0
     elapsed = 0.0
+    parts = {"project_q": 0.0, "score_blocks": 0.0, "rank_victims": 0.0}
     while elapsed < budget_s:
         li, s, slots = rows[done % len(rows)]
         t0 = time.perf_counter()
         predictor.project_q(q_all[l0 + li, s], P)
+        t1 = time.perf_counter()
         sc = predictor.score_one(qp_all[li, s], slots)
+        t2 = time.perf_counter()
         predictor.rank_victims(sc.astype(np.float32)[None])
-        elapsed += time.perf_counter() - t0
+        t3 = time.perf_counter()
+        parts["project_q"] += t1 - t0
+        parts["score_blocks"] += t2 - t1
+        parts["rank_victims"] += t3 - t2
+        elapsed += t3 - t0
         done += 1
         blocks += c.n
     threads = 1
@@ -90,9 +97,17 @@ def cpu_baseline(wl, budget_s=12.0):
     except Exception:
         pass
     gbs = blocks * c.slot_bytes / elapsed / 1e9
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "blocks_per_s": round(blocks / elapsed, 1), "seconds": round(elapsed, 2),
-            "host_cpus": len(os.sched_getaffinity(0)),
+            "seconds_per_part": {k: round(v, 3) for k, v in parts.items()},
+            "rank_keys_per_s": round(blocks / parts["rank_victims"], 1) if parts["rank_victims"] > 0 else None,
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model,
             "sample": f"{done} (layer, sequence) score rows of {c.n} blocks each (project_q + score_blocks + "
                       f"rank_victims, float64 NumPy on the GPU's own q_proj and A_g), cycling over "
                       f"{len(rows)} distinct rows of the same workload"}
@@ -336,6 +351,8 @@ def main():
         "roofline": roofline,
     }
     out["step_breakdown_median_us"] = breakdown
+    # ranking: keys ordered per second (every (layer, sequence) row of n blocks)
+    out["rank_keys_per_s"] = round(nl * c.S * c.n / (breakdown["rank_victims"] * 1e-6), 1)
     if per_layer is not None:
         out["score_per_layer_call"] = per_layer
     out["step_wall_us"] = fused_us
