@@ -25,8 +25,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (PRED_FLAG_ZERO_AG, dims, pred_create, pred_destroy, pred_project_kv_block,  # noqa: F401
-               pred_project_q, pred_rank_victims, pred_rank_workspace_bytes, pred_score_blocks,
-               pred_score_rows, pred_select_keep)
+               pred_project_q, pred_project_step, pred_rank_victims, pred_rank_workspace_bytes,
+               pred_score_blocks, pred_score_rows, pred_select_keep)
 from . import synth
 
 
@@ -203,8 +203,8 @@ class Workload:
     def step(self, l0=0, stream=None):
         c = self.cfg
         nl = c.step_layers
-        pred_project_kv_block(self.h, l0, self.k_new[l0:l0 + nl], self.table_new[l0:l0 + nl], stream=stream)
-        pred_project_q(self.h, self.q[l0:l0 + nl], self.q_proj, stream=stream)
+        pred_project_step(self.h, l0, self.k_new[l0:l0 + nl], self.table_new[l0:l0 + nl], self.q[l0:l0 + nl],
+                          self.q_proj, stream=stream)
         pred_score_blocks(self.h, l0, self.q_proj, self.tables, self.scores, stream=stream)
         pred_rank_victims(self.h, self.scores.view(nl * c.S, c.n), self.victims, self.workspace, stream=stream)
 

@@ -342,6 +342,36 @@ def test_invalid_table_entries_are_reported():
         assert np.isnan(s[1]) and s[0] == 0.0 and s[2] == 0.0
 
 
+@pytest.mark.parametrize("R,B,n", [(32, 16, 9), (64, 32, 5), (128, 16, 6)])
+def test_invalid_table_entries_matrix_core_decode(R, B, n):
+    """The decode scorer's matrix-core variant (8 queries per kv head): an out-of-range entry gives NaN
+    and raises the error word; its neighbours (in the same wave) keep their scores."""
+    _say("invalid table, decode mfma", R, B, n)
+    N = 12
+    d = rk.dims(1, 16, 2, 64, R, B, N)
+    with rk.Predictor(d, 5, flags=rk.PRED_FLAG_ZERO_AG) as p:
+        assert rk.pred_score_kernel_name(p.handle, 1) == "score_decode_mfma_kernel"
+        rng = np.random.default_rng(R + B)
+        k = _randn_bits(rng, (1, N, B, 2, 64))
+        rk.pred_project_kv_block(p.handle, 0, _to_dev(k))
+        q = _randn_bits(rng, (1, 1, 1, 16, R))
+        tab = rng.permutation(N)[:n].astype(np.int32)
+        bad = tab.copy()
+        bad[1], bad[n - 2] = N, -3
+        scores = torch.full((1, 1, n), 7.0, dtype=torch.float32, device="cuda")
+        rk.pred_score_blocks(p.handle, 0, _to_dev(q), _tab_dev(bad[None]), scores)
+        with pytest.raises(rk.PredError) as e:
+            rk.pred_device_error(p.handle)
+        assert e.value.code == rk.PRED_ERR_DEVICE
+        got = scores.cpu().numpy().ravel()
+        a_g = _read_slots(p.handle, d, [(0, b) for b in range(N)])
+        want = predictor.score_blocks(q, a_g, 0, tab[None], n).ravel()
+        ok = np.ones(n, bool)
+        ok[[1, n - 2]] = False
+        assert np.isnan(got[~ok]).all()
+        assert_scores(got[ok], want[ok], R, "valid neighbours")
+
+
 def test_host_side_range_errors():
     d = rk.dims(2, 4, 2, 64, 16, 16, 8)
     with rk.Predictor(d, 3) as p:

@@ -38,6 +38,16 @@ def _workload(n=150, N=600, L=4, S=3, M=1, table="slices"):
     return Workload(c)
 
 
+def _separate_calls(wl):
+    """The step as the four single-purpose entry points, into the workload's own outputs."""
+    c = wl.cfg
+    nl = c.step_layers
+    rk.pred_project_kv_block(wl.h, 0, wl.k_new[:nl], wl.table_new[:nl])
+    rk.pred_project_q(wl.h, wl.q[:nl], wl.q_proj)
+    rk.pred_score_blocks(wl.h, 0, wl.q_proj, wl.tables, wl.scores)
+    rk.pred_rank_victims(wl.h, wl.scores.view(nl * c.S, c.n), wl.victims, wl.workspace)
+
+
 def _step(wl, k, q_proj, scores, victims, fill=None, stream=None):
     c = wl.cfg
     nl = c.step_layers
@@ -52,7 +62,7 @@ def test_decode_step_equals_separate_calls(n, M):
     try:
         c = wl.cfg
         nl, S = c.step_layers, c.S
-        wl.step(0)
+        _separate_calls(wl)
         torch.cuda.synchronize()
         qp = torch.empty_like(wl.q_proj)
         sc = torch.full_like(wl.scores, 3.0)
