@@ -578,7 +578,8 @@ void launch_decode_ns(const ScoreArgs& a, const DecodeGeom& gm, int lpr, int qh,
     }
 }
 
-bool decode_geometry(const ScoreArgs& a, DecodeGeom& gm, int& ns, int& lpr, int& qh) {
+// mfma: the slot count for score_decode_mfma_kernel (4 or 16 only).
+bool decode_geometry(const ScoreArgs& a, DecodeGeom& gm, int& ns, int& lpr, int& qh, bool mfma = false) {
     if (!(a.R == 16 || a.R == 32 || a.R == 64 || a.R == 128)) return false;
     lpr = a.R / 8;
     const int64_t U = (int64_t)a.B * lpr;
@@ -590,8 +591,11 @@ bool decode_geometry(const ScoreArgs& a, DecodeGeom& gm, int& ns, int& lpr, int&
     // than 8 on every decode shape (2.6% on 32 layers x 8192 blocks, more on
     // shapes with few workgroups, where small work items also shorten the
     // drain at the end of the launch).  A region of 512+ chunks takes 16, so
-    // that one load slot never covers less than a whole wave-load.
-    ns = U >= 512 ? 16 : 4;
+    // that one load slot never covers less than a whole wave-load.  At r = 32
+    // with one wave-load per kv region (block_size 16) the vector-ALU kernel
+    // takes 2: 312 vs 315 us for 32 layers x 8192 blocks, the same on 64
+    // sequences x 2048 blocks.
+    ns = U >= 512 ? 16 : ((U == 64 && lpr == 4 && !mfma) ? 2 : 4);
     const int chunks = ns * 64;
     gm.NBW = (int)(chunks / U);
     gm.SPB = U >= 64 ? (int)(U / 64) : 1;
@@ -620,8 +624,10 @@ hipError_t launch_score_decode_or_generic(const ScoreArgs& a, hipStream_t stream
     DecodeGeom gm;
     int ns, lpr, qh;
     if (decode_geometry(a, gm, ns, lpr, qh)) {
+        const bool mfma = decode_mfma_ok(a, gm);
+        if (mfma) decode_geometry(a, gm, ns, lpr, qh, true);
         if (!grid_fits(gm.wgs_per_seq * a.S * a.n_layers)) return hipErrorInvalidConfiguration;
-        if (decode_mfma_ok(a, gm)) {
+        if (mfma) {
             const unsigned grid = (unsigned)(gm.wgs_per_seq * a.S * a.n_layers);
             const int q_bytes = gm.q_chunks * 16;
 #define PRED_DMFMA(RV, NSV) score_decode_mfma_kernel<RV, NSV><<<grid, 256, q_bytes, stream>>>(a, gm)
@@ -639,7 +645,7 @@ hipError_t launch_score_decode_or_generic(const ScoreArgs& a, hipStream_t stream
         }
         if (ns == 16) launch_decode_ns<16>(a, gm, lpr, qh, stream);
         else if (ns == 4) launch_decode_ns<4>(a, gm, lpr, qh, stream);
-        else launch_decode_ns<8>(a, gm, lpr, qh, stream);
+        else launch_decode_qh<4, 2>(a, gm, qh, stream);   // ns == 2: r = 32 only
     } else {
         const int64_t total = (int64_t)a.n_layers * a.S * a.n;
         if (!grid_fits((total + 255) / 256)) return hipErrorInvalidConfiguration;
