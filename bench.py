@@ -25,22 +25,27 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E peak, 8 TB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, 2.5 PFLOP/s
 
 
-def _score_kernel_source_hash():
+# sources of each score kernel family (the recorded counters hold only while these are unchanged)
+_KERNEL_SOURCES = {"score_decode": ["score_decode.hip", "common.h", "kernels.h"],
+                   "score_prefill": ["score_prefill.hip", "common.h", "kernels.h"]}
+
+
+def _score_kernel_source_hash(family="score_decode"):
     h = hashlib.sha256()
-    for f in ["score_decode.hip", "common.h", "kernels.h"]:
+    for f in _KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, "rank_kv_block_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def _traffic(workload, launch_bytes):
+def _traffic(workload, family="score_decode"):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they match the current kernel."""
-    path = os.path.join(ROOT, "profiles", f"score_decode_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{family}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256_16") != _score_kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != _score_kernel_source_hash(family):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -317,13 +322,14 @@ def main():
         flops = 2.0 * nl * c.S * c.M * c.Hq * c.R * c.n * c.B
         achieved = flops / (score_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS,
-                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
+                    "traffic": _traffic(c.name, "score_prefill"),
                     "kernel": kernel, "algorithmic_flops_per_launch": flops,
                     "algorithmic_bytes_per_launch": a_g_bytes + aux_bytes}
     else:
         achieved = a_g_bytes / (score_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic(c.name, a_g_bytes),
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic(c.name),
                     "kernel": kernel, "algorithmic_bytes_per_launch": a_g_bytes,
                     "aux_bytes_per_launch": aux_bytes}
     out = {
