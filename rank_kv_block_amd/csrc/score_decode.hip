@@ -44,6 +44,13 @@
 #ifndef PRED_DECODE_MFMA_MIN_QUERIES
 #define PRED_DECODE_MFMA_MIN_QUERIES 5
 #endif
+// Matrix-core decode with 4 wave-loads per kv region: split each block over
+// two waves of 2 load slots (1) or give each wave a whole block (0).  Split
+// measured 157.5 vs 159.3 us for a 70B-shaped layer (32768 blocks of 32 KiB),
+// in alternating runs on one box (smaller work items shorten the drain).
+#ifndef PRED_DECODE_MFMA_SPLIT
+#define PRED_DECODE_MFMA_SPLIT 1
+#endif
 
 namespace pred {
 
@@ -123,6 +130,7 @@ struct DecodeGeom {
     int n_groups;          // ceil(n_eff / QH)
     int q_chunks;          // 16-byte chunks of one (layer, sequence) q_proj slab [M, Hq, R]
     int64_t wgs_per_seq;   // workgroups per (layer, sequence); a workgroup never spans two
+    int WPB;               // waves per block (2: a block's kv regions split over two waves)
 };
 
 constexpr int kWaves = 4;
@@ -352,7 +360,7 @@ void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
 // own MFMA.  Accumulator lane (n, c) holds rows 4c .. 4c + 3 of column n, i.e.
 // tokens 4c/H .. of the wave-load, so the sums stay inside a lane: token
 // 4c/H + v gets sum over p of C_p[v*H + p].
-template <int R, int NS>
+template <int R, int NS, int WPB>
 __global__ __launch_bounds__(256) void score_decode_mfma_kernel(ScoreArgs a, DecodeGeom gm) {
     constexpr int H = R / 32;             // parts per token row = MFMAs per wave-load
     constexpr int ROWB = R * 2;           // bytes per token row
@@ -365,7 +373,8 @@ __global__ __launch_bounds__(256) void score_decode_mfma_kernel(ScoreArgs a, Dec
     const int64_t ls = blockIdx.x / gm.wgs_per_seq;
     const int s = (int)(ls % a.S);
     const int l = (int)(ls / a.S);
-    const int64_t b_first = (wgb * kWaves + wave_id) * gm.NBW;
+    const int64_t b_first = ((wgb * kWaves + wave_id) / WPB) * gm.NBW;
+    const int pbase = (wave_id % WPB) * NS;   // first wave-load of the block's regions this wave streams
     const uint16_t* qrows = a.qp + ((int64_t)l * a.S + s) * (int64_t)a.M * a.Hq * R;
     const bool has_work = b_first < a.n;
     const int m = lane & 15;
@@ -388,7 +397,7 @@ __global__ __launch_bounds__(256) void score_decode_mfma_kernel(ScoreArgs a, Dec
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl) {
         const int bi = (sl * 64) >> gm.log2U;
-        const int piece = sl - bi * gm.SPB;
+        const int piece = pbase + sl - bi * gm.SPB;
         const int32_t phys = __builtin_amdgcn_readlane(tab_lane, bi);
         const bool ok = bi < gm.NBW && b_first + bi < a.n && phys >= 0 && (int64_t)phys < a.N;
         soff_slot[sl] = (uint32_t)((ok ? (int64_t)phys : 0) * slot_bytes + 1024 * piece);
@@ -454,42 +463,63 @@ __global__ __launch_bounds__(256) void score_decode_mfma_kernel(ScoreArgs a, Dec
         for (int i = threadIdx.x; i < gm.q_chunks; i += 256) q_lds[i] = src[i];
         __syncthreads();
     }
-    if (!has_work) return;   // after the only barrier
-    int kv = 0;
-    for (; kv + 2 < a.Hk; kv += 2) {
-        load_a(A1, kvr(kv + 1));
-        score_kv(A0, kvr(kv));
-        load_a(A0, kvr(kv + 2));
-        score_kv(A1, kvr(kv + 1));
-    }
-    if (kv + 1 < a.Hk) {
-        load_a(A1, kvr(kv + 1));
-        score_kv(A0, kvr(kv));
-        score_kv(A1, kvr(kv + 1));
-    } else {
-        score_kv(A0, kvr(kv));
+    if (WPB == 1 && !has_work) return;   // after the only barrier (a split block meets one more)
+    if (has_work) {
+        int kv = 0;
+        for (; kv + 2 < a.Hk; kv += 2) {
+            load_a(A1, kvr(kv + 1));
+            score_kv(A0, kvr(kv));
+            load_a(A0, kvr(kv + 2));
+            score_kv(A1, kvr(kv + 1));
+        }
+        if (kv + 1 < a.Hk) {
+            load_a(A1, kvr(kv + 1));
+            score_kv(A0, kvr(kv));
+            score_kv(A1, kvr(kv + 1));
+        } else {
+            score_kv(A0, kvr(kv));
+        }
     }
 
     float* out = a.scores + ((int64_t)l * a.S + s) * a.n;
     const int32_t* table = a.tables ? a.tables + (int64_t)s * a.n : nullptr;
-    float acc = -__builtin_inff();
+    auto store = [&](int64_t b, float v) {
+        const int64_t phys = table ? (int64_t)table[b] : b;
+        if (phys >= 0 && phys < a.N) {
+            out[b] = v;
+        } else {
+            out[b] = __uint_as_float(0x7FC00000u);
+            atomicOr(a.err, DEVERR_TABLE);
+        }
+    };
+    if constexpr (WPB > 1) {
+        // one block per wave pair: each wave's max of its half, combined in LDS
+        __shared__ float half_max[kWaves];
+        float acc = -__builtin_inff();
 #pragma unroll
-    for (int sl = 0; sl < NS; ++sl) {
-        acc = fmaxf(acc, rm[sl]);
-        if ((sl + 1) % gm.SPB == 0) {
-            const float v = wave_max_xor(acc, 64);
-            const int bi = sl / gm.SPB;
-            const int64_t b = b_first + bi;
-            if (lane == 0 && bi < gm.NBW && b < a.n) {
-                const int64_t phys = table ? (int64_t)table[b] : b;
-                if (phys >= 0 && phys < a.N) {
-                    out[b] = v;
-                } else {
-                    out[b] = __uint_as_float(0x7FC00000u);
-                    atomicOr(a.err, DEVERR_TABLE);
-                }
+        for (int sl = 0; sl < NS; ++sl) acc = fmaxf(acc, rm[sl]);
+        acc = wave_max_xor(acc, 64);
+        if (lane == 0) half_max[wave_id] = acc;
+        __syncthreads();
+        if (has_work && lane == 0 && wave_id % WPB == 0) {
+            float v = half_max[wave_id];
+#pragma unroll
+            for (int w = 1; w < WPB; ++w) v = fmaxf(v, half_max[wave_id + w]);
+            store(b_first, v);
+        }
+        return;
+    } else {
+        float acc = -__builtin_inff();
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+            acc = fmaxf(acc, rm[sl]);
+            if ((sl + 1) % gm.SPB == 0) {
+                const float v = wave_max_xor(acc, 64);
+                const int bi = sl / gm.SPB;
+                const int64_t b = b_first + bi;
+                if (lane == 0 && bi < gm.NBW && b < a.n) store(b, v);
+                acc = -__builtin_inff();
             }
-            acc = -__builtin_inff();
         }
     }
 }
@@ -596,7 +626,12 @@ bool decode_geometry(const ScoreArgs& a, DecodeGeom& gm, int& ns, int& lpr, int&
     // takes 2: 312 vs 315 us for 32 layers x 8192 blocks, the same on 64
     // sequences x 2048 blocks.
     ns = U >= 512 ? 16 : ((U == 64 && lpr == 4 && !mfma) ? 2 : 4);
-    const int chunks = ns * 64;
+    gm.WPB = 1;
+    if (mfma && U == 256 && PRED_DECODE_MFMA_SPLIT) {
+        ns = 2;
+        gm.WPB = 2;
+    }
+    const int chunks = ns * 64 * gm.WPB;
     gm.NBW = (int)(chunks / U);
     gm.SPB = U >= 64 ? (int)(U / 64) : 1;
     const int g = a.Hq / a.Hk;
@@ -604,7 +639,7 @@ bool decode_geometry(const ScoreArgs& a, DecodeGeom& gm, int& ns, int& lpr, int&
     qh = pick_qh(gm.n_eff);
     gm.n_groups = (gm.n_eff + qh - 1) / qh;
     gm.q_chunks = (int)((int64_t)a.M * a.Hq * a.R / 8);
-    const int64_t waves_per_seq = (a.n + gm.NBW - 1) / gm.NBW;
+    const int64_t waves_per_seq = (a.n + gm.NBW - 1) / gm.NBW * gm.WPB;
     gm.wgs_per_seq = (waves_per_seq + kWaves - 1) / kWaves;
     return true;
 }
@@ -630,8 +665,12 @@ hipError_t launch_score_decode_or_generic(const ScoreArgs& a, hipStream_t stream
         if (mfma) {
             const unsigned grid = (unsigned)(gm.wgs_per_seq * a.S * a.n_layers);
             const int q_bytes = gm.q_chunks * 16;
-#define PRED_DMFMA(RV, NSV) score_decode_mfma_kernel<RV, NSV><<<grid, 256, q_bytes, stream>>>(a, gm)
-            if (ns == 16) {
+#define PRED_DMFMA(RV, NSV) score_decode_mfma_kernel<RV, NSV, 1><<<grid, 256, q_bytes, stream>>>(a, gm)
+            if (gm.WPB == 2) {
+                if (a.R == 64) score_decode_mfma_kernel<64, 2, 2><<<grid, 256, q_bytes, stream>>>(a, gm);
+                else if (a.R == 128) score_decode_mfma_kernel<128, 2, 2><<<grid, 256, q_bytes, stream>>>(a, gm);
+                else score_decode_mfma_kernel<32, 2, 2><<<grid, 256, q_bytes, stream>>>(a, gm);
+            } else if (ns == 16) {
                 if (a.R == 32) PRED_DMFMA(32, 16);
                 else if (a.R == 64) PRED_DMFMA(64, 16);
                 else PRED_DMFMA(128, 16);
