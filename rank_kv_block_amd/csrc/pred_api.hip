@@ -183,8 +183,10 @@ int pred_check_fit(const pred_dims* d, uint64_t free_bytes) {
 
 const char* pred_limits(void) {
     return "head_dim and r multiples of 8; r <= 256; head_dim <= 65536; 16-byte aligned q, q_proj and k "
-           "buffers. Streaming decode scorer: r in {16,32,64,128} and block_size*r/8 a power of two <= 1024; "
-           "other shapes use a plain per-block kernel. Rank: n_blocks <= 2^31-1; above 2048 per segment a "
+           "buffers. Streaming decode scorer: r in {16,32,64,128} and block_size*r/8 a power of two <= 1024 "
+           "(5 to 16 queries per kv head with r in {32,64,128} and block_size*r >= 512: its matrix-core "
+           "variant); other shapes use a plain per-block kernel; more than 16 queries per kv head with r in "
+           "{16,32,64,128} and block_size in {8,16,32}: the many-row MFMA scorer. Rank: n_blocks <= 2^31-1; above 2048 per segment a "
            "workspace of 8*n_blocks*n_segments bytes is needed (16*n_blocks*n_segments above 8192); select_keep "
            "the same with n_blocks = stride, n_segments = rows. Row scorer: MFMA for r in {16,32,64,128}, "
            "block_size in {8,16,32}, num_kv_heads in {1,2,4,8}, num_q_heads a multiple of 4; a plain kernel "

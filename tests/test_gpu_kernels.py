@@ -147,6 +147,10 @@ SHAPES = [
     (1, 8, 8, 64, 32, 32, 40, 27, 1, 5, "perm"),           # g = 1, 5 rows
     (1, 16, 2, 64, 16, 16, 70, 31, 2, 1, "perm"),          # 8 queries at r = 16: vector-ALU decode kernel
     (1, 8, 1, 64, 32, 8, 40, 23, 1, 1, "perm"),            # 8 queries, 512-byte kv regions: vector-ALU kernel
+    # largest shapes the limits allow
+    (1, 8, 2, 64, 256, 16, 30, 13, 1, 1, "perm"),          # r = 256: plain per-block kernel
+    (1, 16, 2, 64, 128, 64, 24, 9, 1, 1, "perm"),          # r = 128, block_size 64: 16 KiB kv regions (U = 1024)
+    (1, 4, 1, 64, 128, 64, 24, 11, 2, 1, "identity"),      # the same with 4 queries: vector-ALU kernel, 16 slots
     (2, 32, 8, 128, 32, 16, 9000, 8200, 1, 1, "perm"),     # larger ragged case, two layers
     (1, 8, 2, 256, 32, 16, 40, 21, 1, 1, "identity"),      # head_dim 256: widest MFMA projection tiles
     (1, 8, 2, 96, 16, 16, 40, 20, 2, 1, "perm"),           # head_dim 96: plain projection kernel
@@ -370,6 +374,32 @@ def test_invalid_table_entries_matrix_core_decode(R, B, n):
         ok[[1, n - 2]] = False
         assert np.isnan(got[~ok]).all()
         assert_scores(got[ok], want[ok], R, "valid neighbours")
+
+
+def test_zero_sized_calls_are_noops():
+    """Every entry point accepts a zero count as a no-op: no error, no write."""
+    d = rk.dims(2, 4, 2, 64, 16, 16, 8)
+    with rk.Predictor(d, 3, flags=rk.PRED_FLAG_ZERO_AG) as p:
+        h = p.handle
+        lib = rk.lib()
+        st = None
+        assert lib.pred_project_q(h, None, 0, None, st) == 0
+        assert lib.pred_project_kv_block(h, 0, 2, None, None, 0, st) == 0
+        assert lib.pred_project_kv_block(h, 0, 0, None, None, 5, st) == 0
+        assert lib.pred_project_step(h, 0, 2, None, None, 0, None, 0, None, st) == 0
+        assert lib.pred_score_blocks(h, 0, 2, None, 1, None, 0, 1, None, st) == 0      # no blocks
+        assert lib.pred_score_blocks(h, 0, 2, None, 1, None, 4, 0, None, st) == 0      # no sequences
+        assert lib.pred_score_blocks(h, 0, 0, None, 1, None, 4, 1, None, st) == 0      # no layers
+        assert lib.pred_rank_victims(h, None, 0, 3, None, None, 0, st) == 0
+        assert lib.pred_rank_victims(h, None, 5, 0, None, None, 0, st) == 0
+        assert lib.pred_select_victims(h, None, 5, 2, 0, None, None, 0, st) == 0
+        assert lib.pred_score_rows(h, 0, None, 0, 0, None, 4, None, 4, st) == 0
+        assert lib.pred_select_keep(h, None, 0, 4, 0, 16, 2, None, None, 0, st) == 0
+        # n_rows = 0 with work to do is an error, not a no-op
+        assert lib.pred_score_blocks(h, 0, 1, None, 0, None, 4, 1, None, st) == rk.PRED_ERR_OUT_OF_RANGE
+        torch.cuda.synchronize()
+        rk.pred_device_error(h)
+        assert not rk.pred_read_slot(h, 0, 0).any()
 
 
 def test_host_side_range_errors():
