@@ -47,7 +47,7 @@
 // Matrix-core decode with 4 wave-loads per kv region: split each block over
 // two waves of 2 load slots (1) or give each wave a whole block (0).  Split
 // measured 157.5 vs 159.3 us for a 70B-shaped layer (32768 blocks of 32 KiB),
-// in alternating runs on one box (smaller work items shorten the drain).
+// in alternating runs on one MI355X (smaller work items shorten the drain).
 #ifndef PRED_DECODE_MFMA_SPLIT
 #define PRED_DECODE_MFMA_SPLIT 1
 #endif
