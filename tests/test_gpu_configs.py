@@ -29,7 +29,8 @@ def _gpu():
     yield
 
 
-def _check_workload(name, l0=0, sample_blocks=128, full_layers=1, keep_per_layer=8, steps=2, side_stream=False):
+def _check_workload(name, l0=0, sample_blocks=128, full_layers=1, keep_per_layer=8, steps=2, side_stream=False,
+                    other_layers_keep=0):
     from rank_kv_block_amd.workloads import CONFIGS, Workload
     import rank_kv_block_amd as rk
     c = CONFIGS[name]
@@ -42,6 +43,13 @@ def _check_workload(name, l0=0, sample_blocks=128, full_layers=1, keep_per_layer
             for b in rng.choice(c.n, min(c.n, keep_per_layer), replace=False):
                 keep.add((l, s, int(b)))
             keep.add((l, s, c.n - 1))          # the block each step re-projects
+    # A_g of layers the step does not score: sampled slots, checked against their keys
+    others = set()
+    for l in range(c.L):
+        if l not in layers:
+            for b in rng.choice(c.n, min(c.n, other_layers_keep), replace=False):
+                others.add((l, 0, int(b)))
+    keep |= others
     _say(name, "setup")
     wl = Workload(c, keep=keep)
     try:
@@ -88,6 +96,12 @@ def _check_workload(name, l0=0, sample_blocks=128, full_layers=1, keep_per_layer
                     idx = np.sort(rng.choice(c.n, min(c.n, sample_blocks), replace=False))
                     want = predictor.score_one(qp[li, s], slots[idx])
                     assert_scores(scores[li, s, idx], want, c.R, f"{name} sampled scores l{l} s{s}")
+        if others:
+            _say(name, "A_g of other layers,", len(others), "slots")
+            kk = sorted(others)
+            k = np.stack([wl.kept[key].view(torch.int16).numpy().view(np.uint16) for key in kk])
+            got = np.stack([rk.pred_read_slot(wl.h, l, int(phys[s, b])) for (l, s, b) in kk])
+            assert_ulp(got, predictor.project_kv_slots(k, P), f"{name} A_g of other layers")
         # ranking (i) on every row: exact against the oracle's sort of the GPU's scores
         want_v = predictor.rank_victims(scores.reshape(nl * c.S, c.n))
         assert np.array_equal(victims, want_v), f"{name}: ranking differs from the oracle's sort"
@@ -124,7 +138,8 @@ def test_config_prefill_chunk():
 
 
 def test_config_long_context_70b():
-    _check_workload("long_context_70b", l0=5, full_layers=1, keep_per_layer=16)
+    # the scored layer in full, plus 24 sampled slots in each of the other 63 layers
+    _check_workload("long_context_70b", l0=5, full_layers=1, keep_per_layer=16, other_layers_keep=24)
 
 
 def test_config_llama3_8b_decode_on_a_second_stream():
