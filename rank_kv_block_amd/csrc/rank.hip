@@ -25,6 +25,10 @@
 //      pairwise, each element finding its place by binary search in the other
 //      run.
 //
+// The k lowest of each row only, for k <= 256 and many rows of 513..2048
+// keys (a prefill chunk's keep sets), take a radix select instead of a sort
+// (select_radix_kernel): the row is never sorted, only its k lowest.
+//
 // The same machinery gives a per-row keep set (qsa_select.rs page, host top-k
 // of a prefill chunk): descending order keys (larger score first, ties still to
 // the lower index) and, per row, only the blocks complete at that row's
@@ -44,6 +48,15 @@ constexpr int kSingle = 2048;        // up to this many keys a segment is sorted
 constexpr int kMergeTPB = 1024;      // step-2 threads per workgroup (one key of its run each)
 constexpr uint32_t kPadKey = 0xFFFFFFFFu;   // padding: above every sort key
 constexpr int kMaxGroup2 = 32768;    // keys of one second-level group (128 KiB of LDS)
+#ifndef PRED_SELECT_MAX_K
+#define PRED_SELECT_MAX_K 256
+#endif
+constexpr int kSelectMaxK = PRED_SELECT_MAX_K;   // radix select for k up to this (the selected keys fill one wave)
+constexpr int kSelectMinN = 512;     // rows up to this length keep the bitonic sort
+// Radix select only pays when the GPU is full of rows (sorting is then
+// throughput-bound): 2048 rows of 2048, top 64: 30.8 vs 40.6 us; with 64 rows
+// the per-row latency of its four histogram passes loses (14.6 vs 11.5 us).
+constexpr int64_t kSelectMinRows = 512;
 
 // Sorting network for one chunk of CH keys (power of two, 256..2048), 4 per
 // thread in blocked order (thread t holds positions 4t .. 4t+3).  Values are
@@ -169,6 +182,125 @@ __global__ __launch_bounds__(CH / 4) void rank_bitonic_kernel(const float* __res
             } else {
                 victims[seg * vstride + off + pos] = (int32_t)(uint32_t)x[e];
             }
+        }
+    }
+}
+
+// The k lowest places of a row of up to 256 * KPT keys, for k <= 256, without
+// sorting the row (the k lowest of each row of a keep-set or victim
+// selection).  One workgroup per row; thread t holds positions t*KPT ..
+// t*KPT + KPT - 1.  Four 8-bit radix-select passes (most significant digit
+// first, LDS histograms of the keys that still match the digits found) find
+// T, the k-th smallest order key, and how many of the keys equal to T the k
+// lowest places hold (want).  Every key below T is taken, and of the keys equal
+// to T the want ones with the lowest positions (a block prefix count over
+// positions), which is exactly the first k places of the (key, position)
+// order.  The k taken (key << 32 | position) composites are then sorted by
+// one wave with the bitonic network above.  Padding keys (a row's entries past
+// its eligible count) are keys like any other and come out as -1.
+template <int KPT>
+__global__ __launch_bounds__(256) void select_radix_kernel(const float* __restrict__ scores, int64_t n, int64_t k,
+                                                           int64_t vstride, RowOrder ro,
+                                                           int32_t* __restrict__ out) {
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t found[2];              // digit, rank wanted inside it
+    __shared__ uint32_t wave_tot[4];
+    __shared__ uint32_t n_sel;
+    __shared__ __align__(16) uint64_t sel[2][256];
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int w = t >> 6;
+    const int64_t seg = blockIdx.x;
+    const float* src = scores + seg * n;
+    const int64_t valid = ro.row_len(seg, n);
+    uint32_t key[KPT];
+    uint32_t present = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int64_t p = (int64_t)t * KPT + j;
+        key[j] = p < valid ? ro.key(src[p]) : kPadKey;
+        present |= (p < n ? 1u : 0u) << j;
+    }
+    if (t == 0) n_sel = 0;
+    uint32_t prefix = 0;
+    uint32_t want = (uint32_t)k;              // rank (1-based) of T among the keys matching prefix
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        const int sh = 24 - 8 * pass;
+        hist[t] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const bool match = ((present >> j) & 1u) && (pass == 0 || (key[j] >> (sh + 8)) == (prefix >> (sh + 8)));
+            if (match) atomicAdd(&hist[(key[j] >> sh) & 255u], 1u);
+        }
+        __syncthreads();
+        if (w == 0) {
+            // lane l owns digits 4l .. 4l+3; exclusive scan of the lane sums
+            const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+            const uint32_t mine = h0 + h1 + h2 + h3;
+            uint32_t incl = mine;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint32_t o = (uint32_t)__shfl_up((int)incl, d);
+                if (lane >= d) incl += o;
+            }
+            uint32_t before = incl - mine;
+            const uint32_t hs[4] = {h0, h1, h2, h3};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (before < want && want <= before + hs[e]) {
+                    found[0] = 4u * lane + e;
+                    found[1] = want - before;
+                }
+                before += hs[e];
+            }
+        }
+        __syncthreads();
+        prefix |= found[0] << sh;
+        want = found[1];
+    }
+    // prefix is T; take every key below it and the first `want` keys equal to it
+    uint32_t eq = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) eq += (((present >> j) & 1u) && key[j] == prefix) ? 1u : 0u;
+    uint32_t incl = eq;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_up((int)incl, d);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) wave_tot[w] = incl;
+    __syncthreads();
+    uint32_t eq_before = incl - eq;
+    for (int v = 0; v < w; ++v) eq_before += wave_tot[v];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        if (!((present >> j) & 1u)) continue;
+        bool take = key[j] < prefix;
+        if (key[j] == prefix) {
+            take = eq_before < want;
+            ++eq_before;
+        }
+        if (take) {
+            const uint32_t slot = atomicAdd(&n_sel, 1u);
+            sel[0][slot] = ((uint64_t)key[j] << 32) | (uint32_t)(t * KPT + j);
+        }
+    }
+    __syncthreads();
+    if (w == 0) {
+        uint64_t x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int pos = 4 * lane + e;
+            x[e] = pos < (int)k ? sel[0][pos] : ~0ull;
+        }
+        int lb = 0;
+        bitonic_ks<256, 2>(x, sel, lb, lane);   // strides below 256: registers and lane exchanges only
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int pos = 4 * lane + e;
+            if (pos < (int)k) out[seg * vstride + pos] = (uint32_t)(x[e] >> 32) == kPadKey ? -1 : (int32_t)(uint32_t)x[e];
         }
     }
 }
@@ -344,6 +476,12 @@ hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int64_t k,
     if (!grid_fits(n_seg * chunks) || !grid_fits(n_seg * ((n + kMaxLdsItems - 1) / kMaxLdsItems) * 8) ||
         !grid_fits((n * n_seg + 255) / 256))
         return hipErrorInvalidConfiguration;
+    if (k <= kSelectMaxK && n > kSelectMinN && n <= kSingle && k < n && n_seg >= kSelectMinRows) {
+        // the k lowest only, many rows: select, then sort k keys
+        if (n <= 1024) select_radix_kernel<4><<<(unsigned)n_seg, 256, 0, st>>>(scores, n, k, k, ro, victims);
+        else select_radix_kernel<8><<<(unsigned)n_seg, 256, 0, st>>>(scores, n, k, k, ro, victims);
+        return hipGetLastError();
+    }
     if (n <= 256) {
         rank_bitonic_kernel<256><<<(unsigned)n_seg, 64, 0, st>>>(scores, n, n, 1, k, k, ro, victims, nullptr, nullptr);
         return hipGetLastError();

@@ -278,10 +278,11 @@ def test_rank_special_orders(kind):
 @pytest.mark.parametrize("n,segs,ks", [(200, 3, (1, 7, 199, 200)), (1000, 2, (1, 64, 999)), (2048, 2, (1, 1024, 2047)),
                                        (5000, 3, (1, 64, 1023, 1024, 1025, 4999)), (8192, 2, (1, 100, 8192)),
                                        (20000, 1, (1, 64, 1024, 8191, 8192, 8193, 19999)),
-                                       (40000, 1, (1, 777, 32768, 39999))])
+                                       (40000, 1, (1, 777, 32768, 39999)),
+                                       (1500, 520, (1, 64, 256, 257)), (600, 512, (1, 255))])   # radix select
 def test_select_exact(n, segs, ks):
     """pred_select_victims: exactly the first k of the full ranking, on every path (one workgroup,
-    chunked with one or two counting-merge levels, pairwise merges)."""
+    chunked with one or two counting-merge levels, pairwise merges, radix select for many rows)."""
     rng = np.random.default_rng(n + 31 * segs)
     s = (rng.integers(-200, 200, size=(segs, n)) * 0.5).astype(np.float32)   # many ties
     s[:, :: 53] = -0.0

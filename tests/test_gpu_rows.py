@@ -161,6 +161,8 @@ KEEP_SHAPES = [
     (4, 5000, 1 << 20, 1, (1, 64, 5000)),                          # chunked, every block complete
     (7, 9000, 4000, 1, (1, 100, 9000)),                            # two merge levels
     (3, 40000, 39990, 1, (1, 1000, 40000)),                        # pairwise merges
+    (600, 2048, 30000, 16, (1, 64, 256, 257)),                     # >= 512 rows, top <= 256: radix select
+    (520, 700, 0, 1, (1, 37, 256, 699)),                           # radix select, rows shorter than top-k
 ]
 
 
