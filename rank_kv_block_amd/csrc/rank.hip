@@ -11,7 +11,8 @@
 // network (rank_bitonic_kernel: registers, in-wave lane exchanges and, for the
 // largest strides only, LDS).  Longer segments use every CU instead of one per
 // segment:
-//   1. chunks of 1024 keys are sorted the same way, one workgroup each, and
+//   1. chunks of 1024 keys are sorted by the same network with two keys per
+//      thread (rank_bitonic2_kernel, 512 threads), one workgroup each, and
 //      written as sorted runs of keys and of their indexes;
 //   2. runs are merged in groups of up to 8192 keys by counting: one workgroup
 //      per run loads its group's keys into LDS, and each element's place in the
@@ -48,6 +49,13 @@ constexpr int kSingle = 2048;        // up to this many keys a segment is sorted
 constexpr int kMergeTPB = 1024;      // step-2 threads per workgroup (one key of its run each)
 constexpr uint32_t kPadKey = 0xFFFFFFFFu;   // padding: above every sort key
 constexpr int kMaxGroup2 = 32768;    // keys of one second-level group (128 KiB of LDS)
+// chunk sort of the chunked path with two keys per thread (1) or four (0):
+// two waves per SIMD instead of one; 32 rows of 8192 keys ranked in 17.5-17.9
+// vs 19.2-19.3 us, one row of 32768 in 21.6-22.0 vs 22.4-22.9 us (alternating
+// runs on one MI355X)
+#ifndef PRED_RANK_CHUNK_2KEYS
+#define PRED_RANK_CHUNK_2KEYS 1
+#endif
 #ifndef PRED_SELECT_MAX_K
 #define PRED_SELECT_MAX_K 256
 #endif
@@ -141,6 +149,95 @@ template <int CH, int K>
 __device__ inline void bitonic_ks(uint64_t (&x)[4], uint64_t (*xb)[CH], int& lb, int t) {
     bitonic_js<CH, K, K / 2>(x, xb, lb, t);
     if constexpr (K < CH) bitonic_ks<CH, K * 2>(x, xb, lb, t);
+}
+
+// The same network with two keys per thread (thread t holds positions 2t and
+// 2t + 1), so a chunk of CH keys takes CH / 2 threads: twice the waves of the
+// four-key version for the same chunk, for chunks whose workgroups would
+// otherwise leave one wave per SIMD.  J = 1 pairs the two registers; J = 2 ..
+// 64 pair lanes (distance J / 2); J >= 128 pairs waves through LDS.
+template <int CH, int K, int J>
+__device__ inline void bitonic2_stage(uint64_t (&x)[2], uint64_t (*xb)[CH], int& lb, int t) {
+    const int lane = t & 63;
+    const int w = t >> 6;
+    const bool asc = ((2 * t) & K) == 0;   // K >= 2: the same for the thread's two positions
+    if constexpr (J == 1) {
+        const uint64_t a = x[0], b = x[1];
+        const uint64_t lo = a < b ? a : b, hi = a < b ? b : a;
+        x[0] = asc ? lo : hi;
+        x[1] = asc ? hi : lo;
+    } else {
+        uint64_t y[2];
+        bool lower;
+        if constexpr (J < 128) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) y[e] = lane_xor_u64<J / 2>(x[e]);
+            lower = (lane & (J / 2)) == 0;
+        } else {
+            uint64_t* buf = xb[lb];
+            *reinterpret_cast<uint4*>(&buf[2 * t]) = make_uint4((uint32_t)x[0], (uint32_t)(x[0] >> 32),
+                                                                (uint32_t)x[1], (uint32_t)(x[1] >> 32));
+            __syncthreads();
+            const int pt = t ^ (J / 2);   // partner thread, the same two offsets
+            const uint4 u = *reinterpret_cast<const uint4*>(&buf[2 * pt]);
+            y[0] = ((uint64_t)u.y << 32) | u.x;
+            y[1] = ((uint64_t)u.w << 32) | u.z;
+            lb ^= 1;
+            lower = (w & (J / 128)) == 0;
+        }
+        const bool keep_min = lower == asc;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const uint64_t a = x[e], b = y[e];
+            x[e] = (keep_min == (a < b)) ? a : b;
+        }
+    }
+}
+
+template <int CH, int K, int J>
+__device__ inline void bitonic2_js(uint64_t (&x)[2], uint64_t (*xb)[CH], int& lb, int t) {
+    bitonic2_stage<CH, K, J>(x, xb, lb, t);
+    if constexpr (J > 1) bitonic2_js<CH, K, J / 2>(x, xb, lb, t);
+}
+
+template <int CH, int K>
+__device__ inline void bitonic2_ks(uint64_t (&x)[2], uint64_t (*xb)[CH], int& lb, int t) {
+    bitonic2_js<CH, K, K / 2>(x, xb, lb, t);
+    if constexpr (K < CH) bitonic2_ks<CH, K * 2>(x, xb, lb, t);
+}
+
+// Sorted runs of CH keys (step 1 of the chunked path) with two keys per
+// thread; writes only each run's first klim places.
+template <int CH>
+__global__ __launch_bounds__(CH / 2) void rank_bitonic2_kernel(const float* __restrict__ scores, int64_t n,
+                                                               int nchunks, int64_t klim, RowOrder ro,
+                                                               uint32_t* __restrict__ run_keys,
+                                                               uint32_t* __restrict__ run_idx) {
+    __shared__ __align__(16) uint64_t xb[2][CH];
+    const int t = threadIdx.x;
+    const int64_t seg = blockIdx.x / nchunks;
+    const int64_t off = (int64_t)(blockIdx.x % nchunks) * CH;
+    const int len = (int)((n - off) < CH ? (n - off) : CH);
+    const float* src = scores + seg * n + off;
+    const int64_t valid = ro.row_len(seg, n);
+    uint64_t x[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int pos = 2 * t + e;
+        x[e] = (pos < len && off + pos < valid) ? (((uint64_t)ro.key(src[pos]) << 32) | (uint32_t)(off + pos))
+                                                : ~0ull;
+    }
+    int lb = 0;
+    bitonic2_ks<CH, 2>(x, xb, lb, t);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int pos = 2 * t + e;
+        if (pos < len && pos < klim) {
+            const int64_t o = seg * n + off + pos;
+            run_keys[o] = (uint32_t)(x[e] >> 32);
+            run_idx[o] = (uint32_t)x[e];
+        }
+    }
 }
 
 // One workgroup per (segment, chunk) of up to CH keys.  Only the first klim
@@ -502,8 +599,12 @@ hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int64_t k,
     uint32_t* bk = ai + total;
     uint32_t* bi = bk + total;
     const int nruns = (int)((n + kChunk - 1) / kChunk);
+#if PRED_RANK_CHUNK_2KEYS
+    rank_bitonic2_kernel<kChunk><<<(unsigned)(n_seg * nruns), kChunk / 2, 0, st>>>(scores, n, nruns, k, ro, ak, ai);
+#else
     rank_bitonic_kernel<kChunk><<<(unsigned)(n_seg * nruns), kChunk / 4, 0, st>>>(scores, n, kChunk, nruns, k, k,
                                                                                 ro, nullptr, ak, ai);
+#endif
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // runs of 1024 -> groups of 8192 (the whole row when it is no longer)
