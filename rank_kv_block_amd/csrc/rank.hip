@@ -9,7 +9,8 @@
 //
 // A segment of up to 2048 keys is sorted inside one workgroup by a bitonic
 // network (rank_bitonic_kernel: registers, in-wave lane exchanges and, for the
-// largest strides only, LDS).  Longer segments use every CU instead of one per
+// largest strides only, LDS; above 1024 keys rank_bitonic2_kernel, the same
+// network with two keys per thread and twice the waves).  Longer segments use every CU instead of one per
 // segment:
 //   1. chunks of 1024 keys are sorted by the same network with two keys per
 //      thread (rank_bitonic2_kernel, 512 threads), one workgroup each, and
@@ -55,6 +56,12 @@ constexpr int kMaxGroup2 = 32768;    // keys of one second-level group (128 KiB 
 // runs on one MI355X)
 #ifndef PRED_RANK_CHUNK_2KEYS
 #define PRED_RANK_CHUNK_2KEYS 1
+#endif
+// one-workgroup sort of rows of 1025..2048 keys with two keys per thread (1)
+// or four (0): 64 rows of 2048 keys 11.8-12.1 vs 13.2-13.5 us, one row 10.9 vs
+// 11.7 us (alternating runs on one MI355X)
+#ifndef PRED_RANK_SINGLE_2KEYS
+#define PRED_RANK_SINGLE_2KEYS 1
 #endif
 #ifndef PRED_SELECT_MAX_K
 #define PRED_SELECT_MAX_K 256
@@ -206,11 +213,14 @@ __device__ inline void bitonic2_ks(uint64_t (&x)[2], uint64_t (*xb)[CH], int& lb
     if constexpr (K < CH) bitonic2_ks<CH, K * 2>(x, xb, lb, t);
 }
 
-// Sorted runs of CH keys (step 1 of the chunked path) with two keys per
-// thread; writes only each run's first klim places.
+// rank_bitonic_kernel with two keys per thread: sorted runs of CH keys (step
+// 1 of the chunked path), or with run_keys null a whole segment of up to CH
+// keys straight to victims (row stride vstride); only the first klim places
+// are written.
 template <int CH>
 __global__ __launch_bounds__(CH / 2) void rank_bitonic2_kernel(const float* __restrict__ scores, int64_t n,
-                                                               int nchunks, int64_t klim, RowOrder ro,
+                                                               int nchunks, int64_t klim, int64_t vstride,
+                                                               RowOrder ro, int32_t* __restrict__ victims,
                                                                uint32_t* __restrict__ run_keys,
                                                                uint32_t* __restrict__ run_idx) {
     __shared__ __align__(16) uint64_t xb[2][CH];
@@ -233,9 +243,13 @@ __global__ __launch_bounds__(CH / 2) void rank_bitonic2_kernel(const float* __re
     for (int e = 0; e < 2; ++e) {
         const int pos = 2 * t + e;
         if (pos < len && pos < klim) {
-            const int64_t o = seg * n + off + pos;
-            run_keys[o] = (uint32_t)(x[e] >> 32);
-            run_idx[o] = (uint32_t)x[e];
+            if (run_keys) {
+                const int64_t o = seg * n + off + pos;
+                run_keys[o] = (uint32_t)(x[e] >> 32);
+                run_idx[o] = (uint32_t)x[e];
+            } else {
+                victims[seg * vstride + off + pos] = (int32_t)(uint32_t)x[e];
+            }
         }
     }
 }
@@ -588,7 +602,11 @@ hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int64_t k,
         return hipGetLastError();
     }
     if (n <= kSingle) {
+#if PRED_RANK_SINGLE_2KEYS
+        rank_bitonic2_kernel<2048><<<(unsigned)n_seg, 1024, 0, st>>>(scores, n, 1, k, k, ro, victims, nullptr, nullptr);
+#else
         rank_bitonic_kernel<2048><<<(unsigned)n_seg, 512, 0, st>>>(scores, n, n, 1, k, k, ro, victims, nullptr, nullptr);
+#endif
         return hipGetLastError();
     }
     // workspace: buffer A = run keys then run indexes (4 + 4 bytes per key), and
@@ -600,7 +618,8 @@ hipError_t launch_rank(const float* scores, int64_t n, int64_t n_seg, int64_t k,
     uint32_t* bi = bk + total;
     const int nruns = (int)((n + kChunk - 1) / kChunk);
 #if PRED_RANK_CHUNK_2KEYS
-    rank_bitonic2_kernel<kChunk><<<(unsigned)(n_seg * nruns), kChunk / 2, 0, st>>>(scores, n, nruns, k, ro, ak, ai);
+    rank_bitonic2_kernel<kChunk><<<(unsigned)(n_seg * nruns), kChunk / 2, 0, st>>>(scores, n, nruns, k, k, ro,
+                                                                                 nullptr, ak, ai);
 #else
     rank_bitonic_kernel<kChunk><<<(unsigned)(n_seg * nruns), kChunk / 4, 0, st>>>(scores, n, kChunk, nruns, k, k,
                                                                                 ro, nullptr, ak, ai);
