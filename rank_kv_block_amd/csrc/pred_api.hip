@@ -122,15 +122,16 @@ int create_impl(const pred_dims* d, const uint16_t* p_host_in, uint64_t seed, ui
 
     pred_t* p = new pred_t();
     p->d = *d;
-    hipGetDevice(&p->device);
+    // frees on a failure path: their own errors cannot change the outcome
     auto cleanup = [&](int code) {
-        if (p->p_dev) hipFree(p->p_dev);
-        if (p->pf_dev) hipFree(p->pf_dev);
-        if (p->ag_dev) hipFree(p->ag_dev);
-        if (p->err_dev) hipFree(p->err_dev);
+        if (p->p_dev) (void)hipFree(p->p_dev);
+        if (p->pf_dev) (void)hipFree(p->pf_dev);
+        if (p->ag_dev) (void)hipFree(p->ag_dev);
+        if (p->err_dev) (void)hipFree(p->err_dev);
         delete p;
         return code;
     };
+    if ((e = hipGetDevice(&p->device)) != hipSuccess) return cleanup(hip_fail(e, "hipGetDevice"));
     if ((e = pred::rank_prepare()) != hipSuccess) return cleanup(hip_fail(e, "ranking kernel set-up"));
     if ((e = hipMalloc(&p->p_dev, (size_t)pn * 2)) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(P)"));
     if ((e = hipMalloc(&p->pf_dev, (size_t)pn * 8)) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(P f64)"));
@@ -207,15 +208,17 @@ int pred_create_with_projection(const pred_dims* d, const pred_bf16* p_host, uin
 
 void pred_destroy(pred_t* p) {
     if (!p) return;
+    // best effort: pred_destroy has no way to report a failure, and every
+    // allocation is released whatever the earlier calls return
     int cur = 0;
-    hipGetDevice(&cur);
-    hipSetDevice(p->device);
-    hipDeviceSynchronize();
-    hipFree(p->p_dev);
-    hipFree(p->pf_dev);
-    hipFree(p->ag_dev);
-    hipFree(p->err_dev);
-    hipSetDevice(cur);
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    (void)hipSetDevice(p->device);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(p->p_dev);
+    (void)hipFree(p->pf_dev);
+    (void)hipFree(p->ag_dev);
+    (void)hipFree(p->err_dev);
+    if (have_cur) (void)hipSetDevice(cur);
     delete p;
 }
 
