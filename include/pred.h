@@ -214,6 +214,33 @@ int pred_select_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_
  * n_rows < 1. */
 const char* pred_score_kernel_name(pred_t* p, int32_t n_rows);
 
+/* As pred_score_kernel_name, with the kernel's template arguments for a call
+ * of n_blocks blocks per sequence, e.g.
+ * "score_decode_kernel<lanes_per_row=4,queries=4,slots=2,q_in_lds=1,offset=u32,uniform_slots=1>"
+ * (q_in_lds: the q_proj slab of one (layer, sequence) is staged in LDS, which
+ * it is up to 32 KiB; offset: u64 when one layer of A_g is 4 GiB or more).
+ * Host only; the string is thread-local storage valid until the next call on
+ * the same thread.  NULL for a NULL handle, n_rows < 1 or n_blocks < 1. */
+const char* pred_score_kernel_variant(pred_t* p, int32_t n_rows, int64_t n_blocks);
+
+/* Score kernel override, a debugging switch (qsa_select.rs page: the prefill
+ * selection's environment switch that forces its scalar scorer in place of the
+ * tensor-core one).  PRED_SCORE_PATH_AUTO is the library's own choice; _DECODE
+ * routes every pred_score_blocks / pred_score_blocks_masked call through the
+ * vector-ALU streaming decode kernel (or the plain kernel where its layout does
+ * not fit); _GENERIC routes those and pred_score_rows through the plain
+ * per-block / per-cell kernels.  Every path gives the same scores within
+ * float32 rounding.  The initial value comes from the environment variable
+ * PRED_SCORE_PATH (auto, decode or generic), read once per process; the
+ * variable PRED_LOG=1 makes every score launch print one line on stderr naming
+ * its kernel.  Process-wide, not tied to a handle; set it while no other
+ * thread is enqueueing score calls. */
+enum { PRED_SCORE_PATH_AUTO = 0, PRED_SCORE_PATH_DECODE = 1, PRED_SCORE_PATH_GENERIC = 2 };
+/* Returns 0, or PRED_ERR_OUT_OF_RANGE for a value not in the enum above. */
+int pred_set_score_path(int32_t path);
+/* The current PRED_SCORE_PATH_* value (host only, no device needed). */
+int pred_get_score_path(void);
+
 /* Per-row causal block scores of a prefill chunk (qsa_select.rs page, prefill
  * selection: each query row is scored against the blocks complete at its
  * position; the score is the predictor's, predictor.rs page, score_blocks, kept

@@ -12,6 +12,7 @@ import numpy as np
 
 from . import _lib
 from ._lib import (PRED_FLAG_ZERO_AG, PRED_OK, PredDims, ERROR_NAMES,  # noqa: F401
+                   PRED_SCORE_PATH_AUTO, PRED_SCORE_PATH_DECODE, PRED_SCORE_PATH_GENERIC,
                    PRED_ERR_INVALID_DIMS, PRED_ERR_OUT_OF_RANGE, PRED_ERR_OOM, PRED_ERR_UNSUPPORTED,
                    PRED_ERR_NULL_ARG, PRED_ERR_HIP, PRED_ERR_WORKSPACE, PRED_ERR_DEVICE)
 
@@ -309,6 +310,23 @@ def pred_score_kernel_name(h, n_rows=1):
     if name is None:
         raise PredError(PRED_ERR_NULL_ARG if not h else PRED_ERR_OUT_OF_RANGE, pred_last_error())
     return name.decode()
+
+
+def pred_score_kernel_variant(h, n_rows=1, n_blocks=1):
+    """The kernel and template arguments pred_score_blocks runs for n_rows rows and n_blocks blocks."""
+    name = lib().pred_score_kernel_variant(h, n_rows, n_blocks)
+    if name is None:
+        raise PredError(PRED_ERR_NULL_ARG if not h else PRED_ERR_OUT_OF_RANGE, pred_last_error())
+    return name.decode()
+
+
+def pred_set_score_path(path):
+    """Route score calls through one kernel family (PRED_SCORE_PATH_AUTO / _DECODE / _GENERIC)."""
+    return _check(lib().pred_set_score_path(path))
+
+
+def pred_get_score_path():
+    return lib().pred_get_score_path()
 
 
 def pred_copy_projection(h):

@@ -21,6 +21,12 @@ PRED_ERR_DEVICE = -8
 
 PRED_FLAG_ZERO_AG = 1
 
+PRED_NOALLOC_SCRATCH_BYTES = 8 << 20
+
+PRED_SCORE_PATH_AUTO = 0
+PRED_SCORE_PATH_DECODE = 1
+PRED_SCORE_PATH_GENERIC = 2
+
 ERROR_NAMES = {
     PRED_ERR_INVALID_DIMS: "INVALID_DIMS",
     PRED_ERR_OUT_OF_RANGE: "OUT_OF_RANGE",
@@ -67,6 +73,9 @@ SIGNATURES = {
     "pred_rank_victims": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp]),
     "pred_select_victims": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp]),
     "pred_score_kernel_name": (ctypes.c_char_p, [_vp, _i32]),
+    "pred_score_kernel_variant": (ctypes.c_char_p, [_vp, _i32, _i64]),
+    "pred_set_score_path": (ctypes.c_int, [_i32]),
+    "pred_get_score_path": (ctypes.c_int, []),
     "pred_score_rows": (ctypes.c_int, [_vp, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
     "pred_select_keep": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp, _vp, ctypes.c_size_t, _vp]),
     "pred_decode_step": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i64, _i32, _vp,

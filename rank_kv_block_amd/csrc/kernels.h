@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
 #include "common.h"
 
 namespace pred {
@@ -46,9 +48,22 @@ __device__ inline int fill_of(const ScoreArgs& a, int s) {
     const int f = a.fill[s];
     return f < 0 ? 0 : (f > a.B ? a.B : f);
 }
-// Streaming decode scorer when the shape allows it, else a plain per-block kernel.
-hipError_t launch_score_decode_or_generic(const ScoreArgs& a, hipStream_t stream);
-const char* score_decode_path_name(const ScoreArgs& a);
+// Score kernel choices.  AUTO is the library's own choice; the others are a
+// debugging override (PRED_SCORE_PATH, pred_set_score_path) that routes every
+// score call through one kernel family.
+enum : int {
+    SCORE_PATH_AUTO = 0,
+    SCORE_PATH_DECODE = 1,        // vector-ALU streaming decode kernel (plain kernel where its layout does not fit)
+    SCORE_PATH_GENERIC = 2,       // plain per-block kernel
+    SCORE_PATH_DECODE_MFMA = 3,   // (a kind only) matrix-core streaming decode kernel
+    SCORE_PATH_PREFILL = 4        // (a kind only) many-row MFMA kernel
+};
+// Streaming decode scorer when the shape allows it, else a plain per-block
+// kernel; force = SCORE_PATH_AUTO, _DECODE or _GENERIC.
+hipError_t launch_score_decode_or_generic(const ScoreArgs& a, int force, hipStream_t stream);
+const char* score_decode_path_name(const ScoreArgs& a, int force);
+// The kernel and its template arguments, e.g. "score_decode_kernel<lanes_per_row=4,...>".
+std::string score_decode_variant(const ScoreArgs& a, int force);
 
 // ---- per-row causal scores (score_rows.hip) --------------------------------
 struct RowScoreArgs {
@@ -64,8 +79,9 @@ struct RowScoreArgs {
     int Hq, Hk, B, R;
 };
 // Blocks complete at the position of row r: min(n, (first_pos + r + 1) / B).
-hipError_t launch_score_rows(const RowScoreArgs& a, hipStream_t stream);
-const char* score_rows_path_name(const RowScoreArgs& a);
+// force = SCORE_PATH_GENERIC takes the plain per-cell kernel for every shape.
+hipError_t launch_score_rows(const RowScoreArgs& a, int force, hipStream_t stream);
+const char* score_rows_path_name(const RowScoreArgs& a, int force);
 
 // ---- ranking (rank.hip) --------------------------------------------------
 size_t rank_workspace_bytes(int64_t n, int64_t n_seg);

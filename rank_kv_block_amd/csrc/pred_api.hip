@@ -3,8 +3,10 @@
 // (Predictor::new_on_stream, project_q, project_kv_block, score_blocks,
 // a_g_dev_ptr, dims, read_k_lr_slot), batched over blocks, layers, sequences
 // and query rows, plus the victim ranking the page's module doc describes.
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -91,6 +93,47 @@ int check_supported(const pred_dims* d) {
 }
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// Run-time options, read from the environment once per process:
+//   PRED_SCORE_PATH = auto | decode | generic   which score kernel family every
+//       score call takes (auto: the library's choice; decode: the vector-ALU
+//       streaming decode kernel, or the plain kernel where its layout does not
+//       fit; generic: the plain per-block and per-cell kernels).  A debugging
+//       switch: every path computes the same scores within float32 rounding.
+//   PRED_LOG = 1   one line on stderr per score launch naming the kernel.
+// pred_set_score_path changes the first at run time.
+struct Options {
+    std::atomic<int> score_path{PRED_SCORE_PATH_AUTO};
+    bool log = false;
+};
+
+int parse_score_path(const char* v) {
+    if (!v || !*v || !strcmp(v, "auto") || !strcmp(v, "0")) return PRED_SCORE_PATH_AUTO;
+    if (!strcmp(v, "decode") || !strcmp(v, "valu") || !strcmp(v, "1")) return PRED_SCORE_PATH_DECODE;
+    if (!strcmp(v, "generic") || !strcmp(v, "2")) return PRED_SCORE_PATH_GENERIC;
+    fprintf(stderr, "libpred: PRED_SCORE_PATH=%s is not one of auto, decode, generic; using auto\n", v);
+    return PRED_SCORE_PATH_AUTO;
+}
+
+Options& options() {
+    static Options* o = [] {
+        Options* x = new Options();
+        x->score_path.store(parse_score_path(getenv("PRED_SCORE_PATH")));
+        const char* lg = getenv("PRED_LOG");
+        x->log = lg && *lg && strcmp(lg, "0") != 0;
+        return x;
+    }();
+    return *o;
+}
+
+int score_path() { return options().score_path.load(std::memory_order_relaxed); }
+
+// The kernel family a score_blocks call takes: the many-row MFMA scorer when a
+// kv head has more than 16 queries and the shape is one it handles, else the
+// decode or plain kernel (score_decode.hip decides between those).
+bool takes_prefill(const pred::ScoreArgs& a, int path) {
+    return path == PRED_SCORE_PATH_AUTO && (int64_t)a.M * (a.Hq / a.Hk) > 16 && pred::prefill_supported(a);
+}
 
 int create_impl(const pred_dims* d, const uint16_t* p_host_in, uint64_t seed, uint32_t flags, void* stream,
                 pred_t** out) {
@@ -319,9 +362,14 @@ int score_impl(pred_t* p, int32_t layer0, int32_t n_layers, const pred_bf16* q_p
     a.B = p->d.block_size;
     a.R = p->d.r;
     hipError_t e;
-    const int g = a.Hq / a.Hk;
-    if ((int64_t)a.M * g > 16 && pred::prefill_supported(a)) e = pred::launch_score_prefill(a, (hipStream_t)stream);
-    else e = pred::launch_score_decode_or_generic(a, (hipStream_t)stream);
+    const int path = score_path();
+    const bool prefill = takes_prefill(a, path);
+    if (options().log)
+        fprintf(stderr, "libpred: score_blocks layers [%d, %d) seqs %d blocks %lld rows %d -> %s\n", layer0,
+                layer0 + n_layers, n_seqs, (long long)n_blocks, n_rows,
+                prefill ? "score_prefill_kernel" : pred::score_decode_variant(a, path).c_str());
+    if (prefill) e = pred::launch_score_prefill(a, (hipStream_t)stream);
+    else e = pred::launch_score_decode_or_generic(a, path, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "score_blocks launch");
     return ok();
 }
@@ -355,12 +403,15 @@ int pred_score_blocks_masked(pred_t* p, int32_t layer0, int32_t n_layers, const 
                       stream, true);
 }
 
-const char* pred_score_kernel_name(pred_t* p, int32_t n_rows) {
+namespace {
+
+// ScoreArgs carrying the handle's dims and n_rows rows (enough for the kernel choice)
+bool choice_args(pred_t* p, int32_t n_rows, pred::ScoreArgs& a, const char* what) {
     if (!p || n_rows < 1) {
-        fail(p ? PRED_ERR_OUT_OF_RANGE : PRED_ERR_NULL_ARG, "score_kernel_name: %s", p ? "n_rows < 1" : "NULL handle");
-        return nullptr;
+        fail(p ? PRED_ERR_OUT_OF_RANGE : PRED_ERR_NULL_ARG, "%s: %s", what, p ? "n_rows < 1" : "NULL handle");
+        return false;
     }
-    pred::ScoreArgs a{};
+    a = pred::ScoreArgs{};
     a.N = p->d.max_blocks;
     a.n = 1;
     a.n_layers = 1;
@@ -370,9 +421,44 @@ const char* pred_score_kernel_name(pred_t* p, int32_t n_rows) {
     a.Hk = p->d.num_kv_heads;
     a.B = p->d.block_size;
     a.R = p->d.r;
-    if ((int64_t)a.M * (a.Hq / a.Hk) > 16 && pred::prefill_supported(a)) return "score_prefill_kernel";
-    return pred::score_decode_path_name(a);
+    return true;
 }
+
+thread_local std::string g_variant;
+
+}  // namespace
+
+const char* pred_score_kernel_name(pred_t* p, int32_t n_rows) {
+    pred::ScoreArgs a;
+    if (!choice_args(p, n_rows, a, "score_kernel_name")) return nullptr;
+    const int path = score_path();
+    ok();
+    if (takes_prefill(a, path)) return "score_prefill_kernel";
+    return pred::score_decode_path_name(a, path);
+}
+
+const char* pred_score_kernel_variant(pred_t* p, int32_t n_rows, int64_t n_blocks) {
+    pred::ScoreArgs a;
+    if (!choice_args(p, n_rows, a, "score_kernel_variant")) return nullptr;
+    if (n_blocks < 1) {
+        fail(PRED_ERR_OUT_OF_RANGE, "score_kernel_variant: n_blocks < 1");
+        return nullptr;
+    }
+    a.n = n_blocks;
+    const int path = score_path();
+    ok();
+    g_variant = takes_prefill(a, path) ? std::string("score_prefill_kernel") : pred::score_decode_variant(a, path);
+    return g_variant.c_str();
+}
+
+int pred_set_score_path(int32_t path) {
+    if (path != PRED_SCORE_PATH_AUTO && path != PRED_SCORE_PATH_DECODE && path != PRED_SCORE_PATH_GENERIC)
+        return fail(PRED_ERR_OUT_OF_RANGE, "score path %d is not PRED_SCORE_PATH_AUTO, _DECODE or _GENERIC", path);
+    options().score_path.store(path);
+    return ok();
+}
+
+int pred_get_score_path(void) { return score_path(); }
 
 int pred_score_rows(pred_t* p, int32_t layer, const pred_bf16* q_proj, int64_t rows, int64_t first_pos,
                     const int32_t* block_table, int64_t n_blocks, float* scores, int64_t stride, void* stream) {
@@ -408,7 +494,11 @@ int pred_score_rows(pred_t* p, int32_t layer, const pred_bf16* q_proj, int64_t r
     a.Hk = p->d.num_kv_heads;
     a.B = p->d.block_size;
     a.R = p->d.r;
-    hipError_t e = pred::launch_score_rows(a, (hipStream_t)stream);
+    const int path = score_path();
+    if (options().log)
+        fprintf(stderr, "libpred: score_rows layer %d rows %lld blocks %lld -> %s\n", layer, (long long)rows,
+                (long long)n_blocks, pred::score_rows_path_name(a, path));
+    hipError_t e = pred::launch_score_rows(a, path, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "score_rows launch");
     return ok();
 }

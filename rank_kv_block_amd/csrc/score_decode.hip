@@ -322,7 +322,9 @@ void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
             }
         }
     };
-    if constexpr (UNI) {
+    if (gm.U >= 64) {
+        // a kv region spans SPB whole load slots (slot sl holds block sl / SPB,
+        // also without UNI): the block's max runs over its SPB slots
         float acc = -__builtin_inff();
 #pragma unroll
         for (int sl = 0; sl < NS; ++sl) {
@@ -571,16 +573,27 @@ int pick_qh(int n_eff) {
 
 constexpr int kQLdsMaxBytes = 32768;
 
+// Everything the launcher decides for one call: which kernel, its template
+// arguments and its geometry.  The launch and the reported variant name both
+// come from this one decision.
+struct DecodePlan {
+    int kind;        // SCORE_PATH_* of the kernel that runs: generic, decode (vector ALU) or decode_mfma
+    DecodeGeom gm;
+    int ns, lpr, qh; // load slots per wave, lanes per row, queries per register group
+    bool q_lds;      // q_proj slab staged in LDS (it fits in 32 KiB)
+    bool wide;       // a layer's slab is 4 GiB or more (64-bit slab offsets, as without q_lds)
+    bool uni;        // a kv region spans whole wave-loads (wave-uniform slot offsets)
+};
+
 template <int LPR, int QH, int NS>
-void launch_decode_t(const ScoreArgs& a, const DecodeGeom& gm, hipStream_t st) {
+void launch_decode_t(const ScoreArgs& a, const DecodePlan& pl, hipStream_t st) {
+    const DecodeGeom& gm = pl.gm;
     const unsigned grid = (unsigned)(gm.wgs_per_seq * a.S * a.n_layers);
     const int q_bytes = gm.q_chunks * 16;
-    const bool narrow = a.N * (int64_t)a.Hk * a.B * a.R * 2 < (int64_t(1) << 32);
-    const bool uni = gm.U >= 64;
-    if (q_bytes <= kQLdsMaxBytes && narrow) {
-        if (uni) score_decode_kernel<LPR, QH, NS, true, uint32_t, true><<<grid, 256, q_bytes, st>>>(a, gm);
+    if (pl.q_lds && !pl.wide) {
+        if (pl.uni) score_decode_kernel<LPR, QH, NS, true, uint32_t, true><<<grid, 256, q_bytes, st>>>(a, gm);
         else score_decode_kernel<LPR, QH, NS, true, uint32_t, false><<<grid, 256, q_bytes, st>>>(a, gm);
-    } else if (q_bytes <= kQLdsMaxBytes) {
+    } else if (pl.q_lds) {
         score_decode_kernel<LPR, QH, NS, true, uint64_t, false><<<grid, 256, q_bytes, st>>>(a, gm);
     } else {
         score_decode_kernel<LPR, QH, NS, false, uint64_t, false><<<grid, 256, 0, st>>>(a, gm);
@@ -588,27 +601,28 @@ void launch_decode_t(const ScoreArgs& a, const DecodeGeom& gm, hipStream_t st) {
 }
 
 template <int LPR, int NS>
-void launch_decode_qh(const ScoreArgs& a, const DecodeGeom& gm, int qh, hipStream_t st) {
-    switch (qh) {
-        case 1: launch_decode_t<LPR, 1, NS>(a, gm, st); break;
-        case 2: launch_decode_t<LPR, 2, NS>(a, gm, st); break;
-        case 4: launch_decode_t<LPR, 4, NS>(a, gm, st); break;
-        case 8: launch_decode_t<LPR, 8, NS>(a, gm, st); break;
-        default: launch_decode_t<LPR, 16, NS>(a, gm, st); break;
+void launch_decode_qh(const ScoreArgs& a, const DecodePlan& pl, hipStream_t st) {
+    switch (pl.qh) {
+        case 1: launch_decode_t<LPR, 1, NS>(a, pl, st); break;
+        case 2: launch_decode_t<LPR, 2, NS>(a, pl, st); break;
+        case 4: launch_decode_t<LPR, 4, NS>(a, pl, st); break;
+        case 8: launch_decode_t<LPR, 8, NS>(a, pl, st); break;
+        default: launch_decode_t<LPR, 16, NS>(a, pl, st); break;
     }
 }
 
 template <int NS>
-void launch_decode_ns(const ScoreArgs& a, const DecodeGeom& gm, int lpr, int qh, hipStream_t st) {
-    switch (lpr) {
-        case 2: launch_decode_qh<2, NS>(a, gm, qh, st); break;
-        case 4: launch_decode_qh<4, NS>(a, gm, qh, st); break;
-        case 8: launch_decode_qh<8, NS>(a, gm, qh, st); break;
-        default: launch_decode_qh<16, NS>(a, gm, qh, st); break;
+void launch_decode_ns(const ScoreArgs& a, const DecodePlan& pl, hipStream_t st) {
+    switch (pl.lpr) {
+        case 2: launch_decode_qh<2, NS>(a, pl, st); break;
+        case 4: launch_decode_qh<4, NS>(a, pl, st); break;
+        case 8: launch_decode_qh<8, NS>(a, pl, st); break;
+        default: launch_decode_qh<16, NS>(a, pl, st); break;
     }
 }
 
-// mfma: the slot count for score_decode_mfma_kernel (4 or 16 only).
+// Geometry of the streaming kernels; mfma: the slot count for
+// score_decode_mfma_kernel (2 with a split block, 4 or 16).
 bool decode_geometry(const ScoreArgs& a, DecodeGeom& gm, int& ns, int& lpr, int& qh, bool mfma = false) {
     if (!(a.R == 16 || a.R == 32 || a.R == 64 || a.R == 128)) return false;
     lpr = a.R / 8;
@@ -644,60 +658,89 @@ bool decode_geometry(const ScoreArgs& a, DecodeGeom& gm, int& ns, int& lpr, int&
     return true;
 }
 
+bool slab_is_narrow(const ScoreArgs& a) { return a.N * (int64_t)a.Hk * a.B * a.R * 2 < (int64_t(1) << 32); }
+
 // The matrix-core scorer takes kv heads with more than 4 queries (at 4 or fewer
 // the dot products cost ~1% of the stream), r a multiple of 32 up to 128, kv
 // regions of whole wave-loads, 32-bit slab offsets and the query slab in LDS.
 bool decode_mfma_ok(const ScoreArgs& a, const DecodeGeom& gm) {
-    const bool narrow = a.N * (int64_t)a.Hk * a.B * a.R * 2 < (int64_t(1) << 32);
-    return (a.R == 32 || a.R == 64 || a.R == 128) && gm.U >= 64 && narrow &&
+    return (a.R == 32 || a.R == 64 || a.R == 128) && gm.U >= 64 && slab_is_narrow(a) &&
            gm.q_chunks * 16 <= kQLdsMaxBytes && gm.n_eff >= PRED_DECODE_MFMA_MIN_QUERIES && gm.n_eff <= 16;
+}
+
+DecodePlan make_plan(const ScoreArgs& a, int force) {
+    DecodePlan pl{};
+    pl.kind = SCORE_PATH_GENERIC;
+    if (force == SCORE_PATH_GENERIC || !decode_geometry(a, pl.gm, pl.ns, pl.lpr, pl.qh)) return pl;
+    pl.kind = SCORE_PATH_DECODE;
+    if (force == SCORE_PATH_AUTO && decode_mfma_ok(a, pl.gm)) {
+        decode_geometry(a, pl.gm, pl.ns, pl.lpr, pl.qh, true);
+        pl.kind = SCORE_PATH_DECODE_MFMA;
+    }
+    pl.q_lds = pl.gm.q_chunks * 16 <= kQLdsMaxBytes;
+    pl.wide = !slab_is_narrow(a);
+    pl.uni = pl.gm.U >= 64 && pl.q_lds && !pl.wide;
+    return pl;
 }
 
 }  // namespace
 
-hipError_t launch_score_decode_or_generic(const ScoreArgs& a, hipStream_t stream) {
-    DecodeGeom gm;
-    int ns, lpr, qh;
-    if (decode_geometry(a, gm, ns, lpr, qh)) {
-        const bool mfma = decode_mfma_ok(a, gm);
-        if (mfma) decode_geometry(a, gm, ns, lpr, qh, true);
-        if (!grid_fits(gm.wgs_per_seq * a.S * a.n_layers)) return hipErrorInvalidConfiguration;
-        if (mfma) {
-            const unsigned grid = (unsigned)(gm.wgs_per_seq * a.S * a.n_layers);
-            const int q_bytes = gm.q_chunks * 16;
-#define PRED_DMFMA(RV, NSV) score_decode_mfma_kernel<RV, NSV, 1><<<grid, 256, q_bytes, stream>>>(a, gm)
-            if (gm.WPB == 2) {
-                if (a.R == 64) score_decode_mfma_kernel<64, 2, 2><<<grid, 256, q_bytes, stream>>>(a, gm);
-                else if (a.R == 128) score_decode_mfma_kernel<128, 2, 2><<<grid, 256, q_bytes, stream>>>(a, gm);
-                else score_decode_mfma_kernel<32, 2, 2><<<grid, 256, q_bytes, stream>>>(a, gm);
-            } else if (ns == 16) {
-                if (a.R == 32) PRED_DMFMA(32, 16);
-                else if (a.R == 64) PRED_DMFMA(64, 16);
-                else PRED_DMFMA(128, 16);
-            } else {
-                if (a.R == 32) PRED_DMFMA(32, 4);
-                else if (a.R == 64) PRED_DMFMA(64, 4);
-                else PRED_DMFMA(128, 4);
-            }
-#undef PRED_DMFMA
-            return hipGetLastError();
-        }
-        if (ns == 16) launch_decode_ns<16>(a, gm, lpr, qh, stream);
-        else if (ns == 4) launch_decode_ns<4>(a, gm, lpr, qh, stream);
-        else launch_decode_qh<4, 2>(a, gm, qh, stream);   // ns == 2: r = 32 only
-    } else {
+hipError_t launch_score_decode_or_generic(const ScoreArgs& a, int force, hipStream_t stream) {
+    const DecodePlan pl = make_plan(a, force);
+    if (pl.kind == SCORE_PATH_GENERIC) {
         const int64_t total = (int64_t)a.n_layers * a.S * a.n;
         if (!grid_fits((total + 255) / 256)) return hipErrorInvalidConfiguration;
         score_generic_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(a);
+        return hipGetLastError();
     }
+    const DecodeGeom& gm = pl.gm;
+    if (!grid_fits(gm.wgs_per_seq * a.S * a.n_layers)) return hipErrorInvalidConfiguration;
+    if (pl.kind == SCORE_PATH_DECODE_MFMA) {
+        const unsigned grid = (unsigned)(gm.wgs_per_seq * a.S * a.n_layers);
+        const int q_bytes = gm.q_chunks * 16;
+#define PRED_DMFMA(RV, NSV) score_decode_mfma_kernel<RV, NSV, 1><<<grid, 256, q_bytes, stream>>>(a, gm)
+        if (gm.WPB == 2) {
+            if (a.R == 64) score_decode_mfma_kernel<64, 2, 2><<<grid, 256, q_bytes, stream>>>(a, gm);
+            else if (a.R == 128) score_decode_mfma_kernel<128, 2, 2><<<grid, 256, q_bytes, stream>>>(a, gm);
+            else score_decode_mfma_kernel<32, 2, 2><<<grid, 256, q_bytes, stream>>>(a, gm);
+        } else if (pl.ns == 16) {
+            if (a.R == 32) PRED_DMFMA(32, 16);
+            else if (a.R == 64) PRED_DMFMA(64, 16);
+            else PRED_DMFMA(128, 16);
+        } else {
+            if (a.R == 32) PRED_DMFMA(32, 4);
+            else if (a.R == 64) PRED_DMFMA(64, 4);
+            else PRED_DMFMA(128, 4);
+        }
+#undef PRED_DMFMA
+        return hipGetLastError();
+    }
+    if (pl.ns == 16) launch_decode_ns<16>(a, pl, stream);
+    else if (pl.ns == 4) launch_decode_ns<4>(a, pl, stream);
+    else launch_decode_qh<4, 2>(a, pl, stream);   // ns == 2: r = 32 only
     return hipGetLastError();
 }
 
-const char* score_decode_path_name(const ScoreArgs& a) {
-    DecodeGeom gm;
-    int ns, lpr, qh;
-    if (!decode_geometry(a, gm, ns, lpr, qh)) return "score_generic_kernel";
-    return decode_mfma_ok(a, gm) ? "score_decode_mfma_kernel" : "score_decode_kernel";
+const char* score_decode_path_name(const ScoreArgs& a, int force) {
+    switch (make_plan(a, force).kind) {
+        case SCORE_PATH_DECODE_MFMA: return "score_decode_mfma_kernel";
+        case SCORE_PATH_DECODE: return "score_decode_kernel";
+        default: return "score_generic_kernel";
+    }
+}
+
+std::string score_decode_variant(const ScoreArgs& a, int force) {
+    const DecodePlan pl = make_plan(a, force);
+    char buf[160];
+    if (pl.kind == SCORE_PATH_GENERIC) return "score_generic_kernel";
+    if (pl.kind == SCORE_PATH_DECODE_MFMA)
+        snprintf(buf, sizeof(buf), "score_decode_mfma_kernel<r=%d,slots=%d,waves_per_block=%d>", a.R, pl.ns,
+                 pl.gm.WPB);
+    else
+        snprintf(buf, sizeof(buf), "score_decode_kernel<lanes_per_row=%d,queries=%d,slots=%d,q_in_lds=%d,offset=%s,"
+                 "uniform_slots=%d>", pl.lpr, pl.qh, pl.ns, pl.q_lds ? 1 : 0, (pl.wide || !pl.q_lds) ? "u64" : "u32",
+                 pl.uni ? 1 : 0);
+    return buf;
 }
 
 }  // namespace pred

@@ -375,11 +375,13 @@ bool rows_mfma_supported(const RowScoreArgs& a) {
 
 }  // namespace
 
-const char* score_rows_path_name(const RowScoreArgs& a) { return rows_mfma_supported(a) ? "mfma" : "generic"; }
+const char* score_rows_path_name(const RowScoreArgs& a, int force) {
+    return force != SCORE_PATH_GENERIC && rows_mfma_supported(a) ? "score_rows_kernel" : "score_rows_generic_kernel";
+}
 
-hipError_t launch_score_rows(const RowScoreArgs& a, hipStream_t st) {
+hipError_t launch_score_rows(const RowScoreArgs& a, int force, hipStream_t st) {
     if (a.rows <= 0 || a.stride <= 0) return hipSuccess;
-    if (!rows_mfma_supported(a) || a.n == 0) {
+    if (force == SCORE_PATH_GENERIC || !rows_mfma_supported(a) || a.n == 0) {
         if (!grid_fits((a.rows * a.stride + 255) / 256)) return hipErrorInvalidConfiguration;
         score_rows_generic_kernel<<<(unsigned)((a.rows * a.stride + 255) / 256), 256, 0, st>>>(a);
         return hipGetLastError();

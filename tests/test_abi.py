@@ -126,3 +126,23 @@ def test_library_projection_equals_oracle_generator(D, R, seed):
 def test_limits_text():
     t = rk.pred_limits()
     assert "multiples of 8" in t and "r <= 256" in t
+
+
+def test_score_path_override_from_environment():
+    """PRED_SCORE_PATH is read once per process (a fresh interpreter per value); pred_set_score_path
+    changes it and rejects values outside the enum.  Host only."""
+    import subprocess
+    import sys
+    code = ("import rank_kv_block_amd as rk; a = rk.pred_get_score_path(); "
+            "rk.pred_set_score_path(rk.PRED_SCORE_PATH_GENERIC); b = rk.pred_get_score_path(); "
+            "rc = rk.lib().pred_set_score_path(9); print(a, b, rc, rk.pred_get_score_path())")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for env_value, want in (("", 0), ("auto", 0), ("decode", 1), ("generic", 2), ("bogus", 0)):
+        env = dict(os.environ, PRED_SCORE_PATH=env_value)
+        out = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True, text=True,
+                             timeout=120)
+        assert out.returncode == 0, out.stderr
+        a, b, rc, last = map(int, out.stdout.split())
+        assert (a, b, rc, last) == (want, 2, rk.PRED_ERR_OUT_OF_RANGE, 2), (env_value, out.stdout)
+        if env_value == "bogus":
+            assert "PRED_SCORE_PATH=bogus" in out.stderr

@@ -429,3 +429,152 @@ def test_oom_is_reported_before_allocation():
         rk.pred_create(d, 1)
     assert e.value.code == rk.PRED_ERR_OOM
     assert "halves A_g" in str(e.value)
+
+
+# ------------------------------------------------- decode scorer variants at their limits
+
+# (dims L, Hq, Hk, D, R, B, N), rows, sequences, blocks, slot ids ("high": most ids above the
+# first 4 GiB of the layer slab), expected kernel variant
+VARIANT_CASES = [
+    # one layer's A_g slab is 4.6 GB: 64-bit slab offsets (4 queries per kv head)
+    ((1, 32, 8, 128, 64, 32, 140000), 1, 1, 600, "high",
+     "score_decode_kernel<lanes_per_row=8,queries=4,slots=4,q_in_lds=1,offset=u64,uniform_slots=0>"),
+    # the same slab with 8 queries per kv head: the matrix-core variant needs 32-bit offsets, so the
+    # vector-ALU kernel takes it
+    ((1, 32, 8, 128, 64, 32, 140000), 2, 1, 300, "high",
+     "score_decode_kernel<lanes_per_row=8,queries=8,slots=4,q_in_lds=1,offset=u64,uniform_slots=0>"),
+    # a (layer, sequence) q_proj slab of 64 KiB (4 rows x 64 heads x r = 128) does not fit the
+    # 32 KiB LDS stage: queries come from global memory
+    ((1, 64, 64, 64, 128, 16, 300), 4, 2, 133, "perm",
+     "score_decode_kernel<lanes_per_row=16,queries=4,slots=4,q_in_lds=0,offset=u64,uniform_slots=0>"),
+    # r = 32, block_size 64, 8 queries per kv head: matrix-core decode with each block's four
+    # wave-loads per kv region split over a pair of waves
+    ((1, 16, 2, 64, 32, 64, 40), 1, 1, 27, "perm",
+     "score_decode_mfma_kernel<r=32,slots=2,waves_per_block=2>"),
+]
+
+
+@pytest.mark.parametrize("case", VARIANT_CASES, ids=[c[5].split("<")[0] + f"-N{c[0][6]}-M{c[1]}-S{c[2]}"
+                                                     for c in VARIANT_CASES])
+def test_decode_variant_parity(case):
+    """Kernel variants that only unusual shapes reach (a layer slab of 4 GiB or more, a q_proj slab
+    above the LDS stage, a block split over two waves): the call takes the intended variant, and A_g,
+    scores and ranking match the oracle.  Only the scored slots are written and read back."""
+    (L, Hq, Hk, D, R, B, N), M, S, n, ids, want_variant = case
+    _say("variant", case)
+    rng = np.random.default_rng([N, M, S, n, R])
+    d = rk.dims(L, Hq, Hk, D, R, B, N)
+    seed = int(rng.integers(0, 2 ** 63))
+    with rk.Predictor(d, seed) as p:
+        assert rk.pred_score_kernel_variant(p.handle, M, n) == want_variant
+        if ids == "high":
+            slab = N * Hk * B * R * 2
+            first_high = -(-(1 << 32) // (Hk * B * R * 2))           # first slot past 4 GiB
+            assert slab > (1 << 32) and first_high < N
+            hi = rng.choice(np.arange(first_high, N), (2 * S * n) // 3, replace=False)
+            lo = rng.choice(first_high, S * n - hi.size, replace=False)
+            phys = rng.permutation(np.concatenate([hi, lo])).astype(np.int32).reshape(S, n)
+        else:
+            phys = rng.permutation(N)[: S * n].astype(np.int32).reshape(S, n)
+        P = prng.projection(D, R, seed)
+        k = _randn_bits(rng, (1, S * n, B, Hk, D))
+        rk.pred_project_kv_block(p.handle, 0, _to_dev(k), _tab_dev(phys.reshape(1, -1)))
+        q = _randn_bits(rng, (1, S, M, Hq, D))
+        qp = torch.empty((1, S, M, Hq, R), dtype=torch.bfloat16, device="cuda")
+        rk.pred_project_q(p.handle, _to_dev(q), qp)
+        scores = torch.empty((1, S, n), dtype=torch.float32, device="cuda")
+        rk.pred_score_blocks(p.handle, 0, qp, _tab_dev(phys), scores)
+        vic = torch.empty((S, n), dtype=torch.int32, device="cuda")
+        ws_b = rk.pred_rank_workspace_bytes(n, S)
+        ws = torch.empty((ws_b // 8 + 1,), dtype=torch.int64, device="cuda") if ws_b else None
+        rk.pred_rank_victims(p.handle, scores.view(S, n), vic, ws)
+        rk.pred_device_error(p.handle)
+        qp_bits = _bits_np(qp)
+        assert_ulp(qp_bits, predictor.project_q(q, P), "q_proj")
+        slots = np.stack([rk.pred_read_slot(p.handle, 0, int(b)) for b in phys.reshape(-1)])
+        assert_ulp(slots, predictor.project_kv_slots(k[0], P), "A_g")
+        slots = slots.reshape(S, n, Hk, B, R)
+        got = scores.cpu().numpy()[0]
+        want = np.stack([predictor.score_one(qp_bits[0, s], slots[s]) for s in range(S)])
+        assert_scores(got, want, R)
+        assert_ranking(vic.cpu().numpy(), got, want, R)
+
+
+# ------------------------------------------------- run-time score path override
+
+OVERRIDE_SHAPES = [
+    # L, Hq, Hk, D, R, B, N, n, S, M: each auto choice in turn
+    (1, 32, 8, 128, 64, 16, 300, 260, 1, 64),    # many-row MFMA scorer
+    (1, 64, 8, 128, 64, 32, 100, 97, 1, 1),      # matrix-core decode
+    (2, 32, 8, 128, 32, 16, 300, 150, 2, 1),     # vector-ALU decode
+]
+
+
+@pytest.mark.parametrize("shape", OVERRIDE_SHAPES, ids=[f"q{s[1]}-kv{s[2]}-r{s[4]}-b{s[5]}-M{s[9]}"
+                                                       for s in OVERRIDE_SHAPES])
+def test_forced_score_paths_agree(shape):
+    """pred_set_score_path routes the same call through the vector-ALU decode kernel or the plain
+    kernel; each forced path's scores match the default path's and the oracle's within the score
+    tolerance, and the kernel name follows the setting."""
+    L, Hq, Hk, D, R, B, N, n, S, M = shape
+    _say("forced paths", shape)
+    rng = np.random.default_rng(list(shape))
+    d = rk.dims(L, Hq, Hk, D, R, B, N)
+    with rk.Predictor(d, 99, flags=rk.PRED_FLAG_ZERO_AG) as p:
+        phys = rng.permutation(N)[: S * n].astype(np.int32).reshape(S, n)
+        k = _randn_bits(rng, (L, S * n, B, Hk, D))
+        rk.pred_project_kv_block(p.handle, 0, _to_dev(k), _tab_dev(np.broadcast_to(phys.reshape(1, -1), (L, S * n))))
+        q = _randn_bits(rng, (L, S, M, Hq, D))
+        qp = torch.empty((L, S, M, Hq, R), dtype=torch.bfloat16, device="cuda")
+        rk.pred_project_q(p.handle, _to_dev(q), qp)
+        tab = _tab_dev(phys)
+        got = {}
+        names = {}
+        assert rk.pred_get_score_path() == rk.PRED_SCORE_PATH_AUTO
+        try:
+            for path in (rk.PRED_SCORE_PATH_AUTO, rk.PRED_SCORE_PATH_DECODE, rk.PRED_SCORE_PATH_GENERIC):
+                rk.pred_set_score_path(path)
+                names[path] = rk.pred_score_kernel_name(p.handle, M)
+                sc = torch.empty((L, S, n), dtype=torch.float32, device="cuda")
+                rk.pred_score_blocks(p.handle, 0, qp, tab, sc)
+                torch.cuda.synchronize()
+                got[path] = sc.cpu().numpy()
+        finally:
+            rk.pred_set_score_path(rk.PRED_SCORE_PATH_AUTO)
+        rk.pred_device_error(p.handle)
+        assert names[rk.PRED_SCORE_PATH_DECODE] == "score_decode_kernel"
+        assert names[rk.PRED_SCORE_PATH_GENERIC] == "score_generic_kernel"
+        with pytest.raises(rk.PredError):
+            rk.pred_set_score_path(7)
+        a_g = _read_slots(p.handle, d, [(l, int(b)) for l in range(L) for b in phys.reshape(-1)])
+        want = predictor.score_blocks(_bits_np(qp), a_g, 0, phys, n)
+        for path, s in got.items():
+            assert_scores(s, want, R, f"scores on path {path} ({names[path]})")
+            assert_scores(s, got[rk.PRED_SCORE_PATH_AUTO], R, f"path {path} against the default path")
+
+
+def test_forced_generic_row_scores():
+    """The override also routes pred_score_rows through its plain per-cell kernel; both agree."""
+    _say("forced rows")
+    Hq, Hk, D, R, B, n, rows = 16, 4, 64, 32, 16, 40, 70
+    rng = np.random.default_rng(3)
+    d = rk.dims(1, Hq, Hk, D, R, B, n)
+    with rk.Predictor(d, 5, flags=rk.PRED_FLAG_ZERO_AG) as p:
+        k = _randn_bits(rng, (1, n, B, Hk, D))
+        rk.pred_project_kv_block(p.handle, 0, _to_dev(k))
+        qp = _to_dev(_randn_bits(rng, (rows, Hq, R), 0.5))
+        first_pos = n * B - rows
+        out = {}
+        try:
+            for path in (rk.PRED_SCORE_PATH_AUTO, rk.PRED_SCORE_PATH_GENERIC):
+                rk.pred_set_score_path(path)
+                sc = torch.empty((rows, n + 3), dtype=torch.float32, device="cuda")
+                rk.pred_score_rows(p.handle, 0, qp, first_pos, None, n, sc)
+                torch.cuda.synchronize()
+                out[path] = sc.cpu().numpy()
+        finally:
+            rk.pred_set_score_path(rk.PRED_SCORE_PATH_AUTO)
+        a, g = out[rk.PRED_SCORE_PATH_AUTO], out[rk.PRED_SCORE_PATH_GENERIC]
+        assert np.array_equal(np.isneginf(a), np.isneginf(g))
+        m = ~np.isneginf(a)
+        assert_scores(g[m], a[m], R, "generic row scores against the MFMA row scorer")
