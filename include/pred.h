@@ -190,6 +190,27 @@ int pred_score_blocks_masked(pred_t* p, int32_t layer0, int32_t n_layers, const 
 int pred_rank_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments,
                       int32_t* victims, void* workspace, size_t ws_bytes, void* stream);
 
+/* pred_rank_victims for callers that cannot allocate or pass a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments (without the workspace), checks and result as
+ * pred_rank_victims; the sorted runs live instead in a static device array of
+ * PRED_NOALLOC_SCRATCH_BYTES bytes that each GPU holds from library load to
+ * process end (its address is found once per device by pred_create).  The call
+ * allocates nothing and makes no memset: every byte of scratch it reads it has
+ * written first in the same call.
+ *   scores   device, [n_segments, n_blocks] float32
+ *   victims  device, [n_segments, n_blocks] int32 output
+ * A shape needing more than PRED_NOALLOC_SCRATCH_BYTES
+ * (pred_rank_workspace_bytes(n_blocks, n_segments) above it, e.g. more than
+ * 1048576 keys in rows of 2049..8192) fails with PRED_ERR_WORKSPACE before
+ * anything is enqueued.  Every call on one GPU shares that GPU's array, across
+ * handles and streams: two calls that can run at the same time on one GPU
+ * (different streams or threads without ordering between them) race and give
+ * wrong rankings; order them on one stream. */
+#define PRED_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int pred_rank_victims_noalloc(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments,
+                              int32_t* victims, void* stream);
+
 /* The k lowest-scored blocks of every segment, in eviction order: row s of
  * victims is exactly the first k entries of pred_rank_victims's row s (scores
  * ascending, equal scores in ascending index order, -0 equal to +0, NaN

@@ -11,7 +11,7 @@ import ctypes
 import numpy as np
 
 from . import _lib
-from ._lib import (PRED_FLAG_ZERO_AG, PRED_OK, PredDims, ERROR_NAMES,  # noqa: F401
+from ._lib import (PRED_FLAG_ZERO_AG, PRED_OK, PredDims, ERROR_NAMES, PRED_NOALLOC_SCRATCH_BYTES,  # noqa: F401
                    PRED_SCORE_PATH_AUTO, PRED_SCORE_PATH_DECODE, PRED_SCORE_PATH_GENERIC,
                    PRED_ERR_INVALID_DIMS, PRED_ERR_OUT_OF_RANGE, PRED_ERR_OOM, PRED_ERR_UNSUPPORTED,
                    PRED_ERR_NULL_ARG, PRED_ERR_HIP, PRED_ERR_WORKSPACE, PRED_ERR_DEVICE)
@@ -220,6 +220,16 @@ def pred_rank_victims(h, scores, victims, workspace=None, stream=None):
     _check(lib().pred_rank_victims(h, _ptr(scores, "scores", (torch.float32,)), n, n_seg,
                                    _ptr(victims, "victims", (torch.int32,)), _ptr(workspace, "workspace"),
                                    ws_bytes, _stream(stream)))
+
+
+def pred_rank_victims_noalloc(h, scores, victims, stream=None):
+    """pred_rank_victims with the library's static device scratch instead of a workspace."""
+    import torch
+    if scores.dim() != 2 or tuple(victims.shape) != tuple(scores.shape):
+        raise ValueError("scores and victims must both be [n_segments, n_blocks]")
+    n_seg, n = scores.shape
+    _check(lib().pred_rank_victims_noalloc(h, _ptr(scores, "scores", (torch.float32,)), n, n_seg,
+                                           _ptr(victims, "victims", (torch.int32,)), _stream(stream)))
 
 
 def pred_select_victims(h, scores, k, victims, workspace=None, stream=None):

@@ -71,6 +71,7 @@ SIGNATURES = {
     "pred_score_blocks": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _i64, _i32, _vp, _vp]),
     "pred_score_blocks_masked": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _i64, _i32, _vp, _vp, _vp]),
     "pred_rank_victims": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp]),
+    "pred_rank_victims_noalloc": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
     "pred_select_victims": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp]),
     "pred_score_kernel_name": (ctypes.c_char_p, [_vp, _i32]),
     "pred_score_kernel_variant": (ctypes.c_char_p, [_vp, _i32, _i64]),

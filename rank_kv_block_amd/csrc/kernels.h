@@ -87,6 +87,12 @@ const char* score_rows_path_name(const RowScoreArgs& a, int force);
 size_t rank_workspace_bytes(int64_t n, int64_t n_seg);
 // Per-device set-up of the ranking kernels (their LDS limits); called by pred_create.
 hipError_t rank_prepare();
+// Static device scratch for callers that cannot allocate: its size, the set-up
+// that finds its address on `device` (that device current; once per device,
+// repeat calls are no-ops) and that address (null before the set-up).
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+hipError_t rank_scratch_prepare(int device);
+void* rank_scratch(int device);
 // Sort order of a ranking row.  Ascending (eviction order): the order key of
 // the score, NaN first.  Descending (a keep set, larger score first): keys
 // flipped inside [0, 0xFF800001] so that they stay below the padding key and

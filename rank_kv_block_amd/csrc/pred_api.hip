@@ -176,6 +176,8 @@ int create_impl(const pred_dims* d, const uint16_t* p_host_in, uint64_t seed, ui
     };
     if ((e = hipGetDevice(&p->device)) != hipSuccess) return cleanup(hip_fail(e, "hipGetDevice"));
     if ((e = pred::rank_prepare()) != hipSuccess) return cleanup(hip_fail(e, "ranking kernel set-up"));
+    if ((e = pred::rank_scratch_prepare(p->device)) != hipSuccess)
+        return cleanup(hip_fail(e, "address of the static ranking scratch"));
     if ((e = hipMalloc(&p->p_dev, (size_t)pn * 2)) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(P)"));
     if ((e = hipMalloc(&p->pf_dev, (size_t)pn * 8)) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(P f64)"));
     if ((e = hipMalloc(&p->err_dev, 4)) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(error word)"));
@@ -536,6 +538,25 @@ int pred_rank_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t 
                       void* workspace, size_t ws_bytes, void* stream) {
     return rank_or_select(p, scores, n_blocks, n_segments, n_blocks, pred::RowOrder{0, 0, 0}, victims, workspace,
                           ws_bytes, stream, "rank_victims");
+}
+
+static_assert(pred::kNoAllocScratchBytes == PRED_NOALLOC_SCRATCH_BYTES, "scratch size differs from pred.h");
+
+int pred_rank_victims_noalloc(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments, int32_t* victims,
+                              void* stream) {
+    if (!p) return fail(PRED_ERR_NULL_ARG, "predictor is NULL");
+    if (n_blocks > 0 && n_segments > 0 && n_blocks <= 2147483647LL && n_segments <= 2147483647LL) {
+        const size_t need = pred::rank_workspace_bytes(n_blocks, n_segments);
+        if (need > pred::kNoAllocScratchBytes)
+            return fail(PRED_ERR_WORKSPACE,
+                        "rank_victims_noalloc: %lld segments of %lld blocks need %zu bytes of scratch, above its "
+                        "%zu-byte static maximum; use pred_rank_victims with a workspace",
+                        (long long)n_segments, (long long)n_blocks, need, pred::kNoAllocScratchBytes);
+    }
+    void* ws = pred::rank_scratch(p->device);
+    if (!ws) return fail(PRED_ERR_HIP, "rank_victims_noalloc: the static scratch of device %d was not set up", p->device);
+    return rank_or_select(p, scores, n_blocks, n_segments, n_blocks, pred::RowOrder{0, 0, 0}, victims, ws,
+                          pred::kNoAllocScratchBytes, stream, "rank_victims_noalloc");
 }
 
 int pred_select_victims(pred_t* p, const float* scores, int64_t n_blocks, int64_t n_segments, int64_t k,

@@ -37,10 +37,43 @@
 // position.  A row's other entries enter as padding keys above every real key;
 // the merges place padding like equal keys and carry index -1 for it, so the
 // slots of a row with fewer eligible blocks than asked for come out as -1.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace pred {
+
+// Device-resident scratch of the no-allocation ranking entry point
+// (pred_rank_victims_noalloc): the sorted runs of a call live here instead of
+// in a caller workspace.  Each GPU holds its own copy from module load to
+// process end.  In host code `scratch` names only a host-side stand-in, so the
+// kernels get the device address found by hipGetSymbolAddress at set-up.
+static __device__ __align__(256) uint64_t scratch[kNoAllocScratchBytes / sizeof(uint64_t)];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t rank_scratch_prepare(int device) {
+    if (device < 0 || device >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[device]) return hipSuccess;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_dev[device] = ptr;
+    return hipSuccess;
+}
+
+void* rank_scratch(int device) {
+    if (device < 0 || device >= kMaxScratchDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch_dev[device];
+}
 
 namespace {
 
