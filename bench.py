@@ -118,6 +118,88 @@ def cpu_baseline(wl, budget_s=12.0):
                       f"{len(rows)} distinct rows of the same workload"}
 
 
+def roofline_of(c, kernel, score_ms):
+    """Roofline of one score launch of workload c from its mean duration: HBM for the decode
+    kernels (algorithmic A_g bytes), bf16 MFMA for the many-row kernel (algorithmic flops)."""
+    nl = c.step_layers
+    a_g_bytes = c.blocks_per_step * c.slot_bytes
+    aux_bytes = c.blocks_per_step * 8 + nl * c.S * c.M * c.Hq * c.R * 2   # table entry + score per block, q_proj
+    if kernel == "score_prefill_kernel":
+        # a contraction: every (query row, head) against every key of every block
+        flops = 2.0 * nl * c.S * c.M * c.Hq * c.R * c.n * c.B
+        achieved = flops / (score_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
+                "traffic": _traffic(c.name, "score_prefill"),
+                "kernel": kernel, "algorithmic_flops_per_launch": flops,
+                "algorithmic_bytes_per_launch": a_g_bytes + aux_bytes}
+    achieved = a_g_bytes / (score_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic(c.name),
+            "kernel": kernel, "algorithmic_bytes_per_launch": a_g_bytes, "aux_bytes_per_launch": aux_bytes}
+
+
+def time_steps(wl, steps, warmup):
+    """Warm up, then time `steps` whole steps (project_step + score_blocks + rank_victims) on
+    torch's current stream: host wall time per step, and each score launch's HIP-event time (ms)."""
+    import torch
+    import rank_kv_block_amd as rk
+    c = wl.cfg
+    nl = c.step_layers
+    for i in range(warmup):
+        wl.step(wl.layer0_for_step(i))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        l0 = wl.layer0_for_step(i)
+        rk.pred_project_step(wl.h, l0, wl.k_new[l0:l0 + nl], wl.table_new[l0:l0 + nl], wl.q[l0:l0 + nl], wl.q_proj)
+        ev[i][0].record(stream)
+        rk.pred_score_blocks(wl.h, l0, wl.q_proj, wl.tables, wl.scores)
+        ev[i][1].record(stream)
+        rk.pred_rank_victims(wl.h, wl.scores.view(nl * c.S, c.n), wl.victims, wl.workspace)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rk.pred_device_error(wl.h)
+    return (t1 - t0) / steps, sorted(a.elapsed_time(b) for a, b in ev)
+
+
+def other_configs(names, steps, warmup):
+    """Each other workload in turn, set up, timed as the headline one (whole step and score kernel)
+    and freed: one entry per workload with its score kernel's roofline."""
+    import rank_kv_block_amd as rk
+    from rank_kv_block_amd.workloads import CONFIGS, Workload
+    out = {}
+    for name in names:
+        c = CONFIGS[name]
+        print(f"[bench] config {name}: {c.description}", file=sys.stderr, flush=True)
+        t_setup = time.perf_counter()
+        wl = Workload(c)
+        setup_s = time.perf_counter() - t_setup
+        try:
+            step_s, each = time_steps(wl, steps, warmup)
+            kernel = rk.pred_score_kernel_name(wl.h, c.M)
+            score_ms = sum(each) / len(each)
+            a_g_bytes = c.blocks_per_step * c.slot_bytes
+            out[name] = {
+                "description": c.description,
+                "a_g_bytes_per_step": a_g_bytes,
+                "ms_per_step": round(step_s * 1e3, 4),
+                "step_a_g_gbs": round(a_g_bytes / step_s / 1e9, 2),
+                "blocks_per_s": round(c.blocks_per_step / step_s, 1),
+                "score_kernel_us": {"mean": round(score_ms * 1e3, 2), "median": round(each[len(each) // 2] * 1e3, 2),
+                                    "min": round(each[0] * 1e3, 2), "max": round(each[-1] * 1e3, 2)},
+                "score_kernel_variant": rk.pred_score_kernel_variant(wl.h, c.M, c.n),
+                "roofline": roofline_of(c, kernel, score_ms),
+                "setup_s": round(setup_s, 2),
+            }
+        finally:
+            wl.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +210,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--per-layer-calls", action="store_true",
                     help="also time the step's layers scored one layer per call (multi-layer workloads)")
+    ap.add_argument("--configs", default="tiny,batched_decode,long_context_70b,prefill_chunk",
+                    help="other workloads timed after the headline one, in the same process (comma list, or "
+                         "'none')")
+    ap.add_argument("--config-steps", type=int, default=20, help="timed steps of each other workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -153,30 +239,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        wl.step(wl.layer0_for_step(i))
-    torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     nl = c.step_layers
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        l0 = wl.layer0_for_step(i)
-        rk.pred_project_step(wl.h, l0, wl.k_new[l0:l0 + nl], wl.table_new[l0:l0 + nl], wl.q[l0:l0 + nl], wl.q_proj)
-        ev[i][0].record(stream)
-        rk.pred_score_blocks(wl.h, l0, wl.q_proj, wl.tables, wl.scores)
-        ev[i][1].record(stream)
-        rk.pred_rank_victims(wl.h, wl.scores.view(nl * c.S, c.n), wl.victims, wl.workspace)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    rk.pred_device_error(wl.h)
-
-    step_s = (t1 - t0) / args.steps
-    score_each = sorted(a.elapsed_time(b) for a, b in ev)
+    print(f"[bench] warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
+    step_s, score_each = time_steps(wl, args.steps, args.warmup)
     score_ms = sum(score_each) / args.steps
 
     # per-call breakdown of a step, in a separate loop so the timed steps above
@@ -314,24 +380,8 @@ def main():
                      "max_us": round(lt[-1] * 1e3, 2), "a_g_gbs_at_median": round(layer_bytes / (med * 1e-3) / 1e9, 1)}
     blocks = c.blocks_per_step
     a_g_bytes = blocks * c.slot_bytes
-    aux_bytes = blocks * 8 + nl * c.S * c.M * c.Hq * c.R * 2      # table entry + score per block, q_proj
     kernel = rk.pred_score_kernel_name(wl.h, c.M)
-    many_row = kernel == "score_prefill_kernel"
-    if many_row:
-        # a contraction: every (query row, head) against every key of every block
-        flops = 2.0 * nl * c.S * c.M * c.Hq * c.R * c.n * c.B
-        achieved = flops / (score_ms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS,
-                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
-                    "traffic": _traffic(c.name, "score_prefill"),
-                    "kernel": kernel, "algorithmic_flops_per_launch": flops,
-                    "algorithmic_bytes_per_launch": a_g_bytes + aux_bytes}
-    else:
-        achieved = a_g_bytes / (score_ms * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic(c.name),
-                    "kernel": kernel, "algorithmic_bytes_per_launch": a_g_bytes,
-                    "aux_bytes_per_launch": aux_bytes}
+    roofline = roofline_of(c, kernel, score_ms)
     out = {
         "metric": "score_blocks A_g GB/s (% of HBM peak) and blocks scored/s, 1 GPU",
         "value": round(a_g_bytes / step_s / 1e9, 2),
@@ -354,6 +404,7 @@ def main():
         "score_kernel_us": {"median": round(score_each[len(score_each) // 2] * 1e3, 2),
                             "min": round(score_each[0] * 1e3, 2), "max": round(score_each[-1] * 1e3, 2)},
         "score_kernel_path": kernel,
+        "score_kernel_variant": rk.pred_score_kernel_variant(wl.h, c.M, c.n),
         "roofline": roofline,
     }
     out["step_breakdown_median_us"] = breakdown
@@ -368,6 +419,17 @@ def main():
         print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     wl.close()
+    others = [n for n in args.configs.split(",") if n and n != "none" and n != c.name]
+    if others:
+        out["configs"] = other_configs(others, args.config_steps, min(args.warmup, 3))
+    del side
+    torch.cuda.synchronize()
+    # this process starts no other process; say so from the process table at the end
+    try:
+        import psutil
+        out["child_processes_at_exit"] = len(psutil.Process().children(recursive=True))
+    except ImportError:
+        pass
     print(json.dumps(out), flush=True)
 
 

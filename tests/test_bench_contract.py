@@ -28,8 +28,9 @@ def test_bench_json_line():
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    print("[case] bench.py --config tiny", flush=True)
-    r = _run(["--config", "tiny", "--steps", "3", "--warmup", "1", "--cpu-budget", "0.5"], 300)
+    print("[case] bench.py --config tiny --configs batched_decode", flush=True)
+    r = _run(["--config", "tiny", "--steps", "3", "--warmup", "1", "--cpu-budget", "0.5", "--configs",
+              "batched_decode", "--config-steps", "2"], 300)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.strip()]
     assert len(lines) == 1, r.stdout
@@ -48,3 +49,9 @@ def test_bench_json_line():
     assert rl["kernel"] == "score_decode_kernel"
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    # the other workloads, timed after the headline one in the same process
+    cfg = d["configs"]["batched_decode"]
+    assert cfg["ms_per_step"] > 0 and cfg["score_kernel_us"]["median"] > 0
+    assert cfg["roofline"]["bound"] == "hbm" and cfg["roofline"]["kernel"] == "score_decode_kernel"
+    assert cfg["score_kernel_variant"].startswith("score_decode_kernel<")
+    assert d["child_processes_at_exit"] == 0
