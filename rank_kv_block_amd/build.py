@@ -27,7 +27,14 @@ EXTRA = {
     "prng.cpp": ["-ffp-contract=off", "-fno-fast-math"],
     # MFMA results straight into VGPRs: the max epilogue then reads them without
     # accumulator-register copies
-    "score_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "score_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+    # The MFMA scorers take maxima of MFMA results.  Without NaN semantics fmaxf
+    # is a plain v_max3_f32; with them every operand the compiler cannot prove
+    # quiet first goes through a canonicalising v_max_f32 (one more instruction
+    # per element), and the NaN-propagating maximum (v_maximum3_f32) measured
+    # slower than both.  These files write NaN only as integer bit patterns, and
+    # a NaN product (a slot holding non-finite keys) gives an unspecified score.
+    "score_rows.hip": ["-fno-honor-nans"],
 }
 
 

@@ -92,9 +92,5 @@ __device__ inline float lane_xor(float v) {
     return __shfl_xor(v, M);
 }
 
-__device__ inline float key_to_float(uint32_t k) {
-    if (k == 0u) return __uint_as_float(0x7FC00000u);
-    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
-}
 
 }  // namespace pred

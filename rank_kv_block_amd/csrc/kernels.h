@@ -77,6 +77,7 @@ struct RowScoreArgs {
     int64_t n;              // blocks of the sequence (table entries)
     int64_t rows, first_pos, stride;
     int Hq, Hk, B, R;
+    int n_cu;               // compute units of the device (the MFMA kernel launches one workgroup per CU)
 };
 // Blocks complete at the position of row r: min(n, (first_pos + r + 1) / B).
 // force = SCORE_PATH_GENERIC takes the plain per-cell kernel for every shape.

@@ -24,6 +24,7 @@ bool prefill_supported(const ScoreArgs& a);
 struct pred_handle {
     pred_dims d;
     int device;
+    int n_cu;          // compute units of that device
     uint16_t* p_dev;   // [D, R] bf16
     double* pf_dev;    // [D, R] float64 copy read by the projection kernels
     uint16_t* ag_dev;  // [L, N, Hk, B, R] bf16
@@ -175,6 +176,8 @@ int create_impl(const pred_dims* d, const uint16_t* p_host_in, uint64_t seed, ui
         return code;
     };
     if ((e = hipGetDevice(&p->device)) != hipSuccess) return cleanup(hip_fail(e, "hipGetDevice"));
+    if ((e = hipDeviceGetAttribute(&p->n_cu, hipDeviceAttributeMultiprocessorCount, p->device)) != hipSuccess)
+        return cleanup(hip_fail(e, "compute unit count"));
     if ((e = pred::rank_prepare()) != hipSuccess) return cleanup(hip_fail(e, "ranking kernel set-up"));
     if ((e = pred::rank_scratch_prepare(p->device)) != hipSuccess)
         return cleanup(hip_fail(e, "address of the static ranking scratch"));
@@ -496,6 +499,7 @@ int pred_score_rows(pred_t* p, int32_t layer, const pred_bf16* q_proj, int64_t r
     a.Hk = p->d.num_kv_heads;
     a.B = p->d.block_size;
     a.R = p->d.r;
+    a.n_cu = p->n_cu;
     const int path = score_path();
     if (options().log)
         fprintf(stderr, "libpred: score_rows layer %d rows %lld blocks %lld -> %s\n", layer, (long long)rows,

@@ -18,9 +18,9 @@
 // query rows); the lane keeps a running max of its column over all query
 // tiles.  At the end the two lane halves are combined, then the 8, 16 or 32
 // lanes of one block, and the block's max goes to the score array with an
-// atomic max on an order-preserving uint32 key (kv heads and query parts sit in
-// different workgroups).  A fill kernel clears the keys first and a last kernel
-// turns them back into float32 in place.
+// integer atomic max (or min) on the float's bit pattern, which orders floats
+// (kv heads and query parts sit in different workgroups).  A fill kernel sets
+// the scores to -inf first.
 //
 // Workgroups are numbered kv-head fastest, so with 8 kv heads each XCD (which
 // takes every 8th workgroup) serves one kv head and its L2 holds one kv head's
@@ -47,9 +47,19 @@ struct PrefillGeom {
     int64_t groups;       // key groups per (layer, sequence, kv head)
 };
 
+// Float max of v into the float at p, on its bit pattern: non-negative floats
+// order as signed integers, negative ones in reverse as unsigned integers, so
+// an integer max (v >= 0) or min (v < 0) is the float max.  A score starts at
+// -inf (0xFF800000), the identity of both.
+__device__ inline void atomic_max_bits(uint32_t* p, float v) {
+    const uint32_t u = __float_as_uint(v);
+    if ((int32_t)u >= 0) atomicMax(reinterpret_cast<int*>(p), (int)u);
+    else atomicMin(p, u);
+}
+
 // R: projected width; NKT: 32-key tiles per wave; BS: block size in tokens.
 template <int R, int NKT, int BS>
-__global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, PrefillGeom gm, uint32_t* __restrict__ keys) {
+__global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, PrefillGeom gm, uint32_t* __restrict__ bits) {
     constexpr int RS = R / 16;                  // MFMA k-steps of 16
     constexpr int CPR = R / 8;                  // 16-byte pieces per query vector
     constexpr int ROWB = R * 2 + 16;            // LDS bytes per query row (16 bytes of padding)
@@ -146,10 +156,10 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, Prefill
         }
 #pragma unroll
         for (int t = 0; t < NKT; ++t) {
-            float m = fmaxf(acc[t][0], acc[t][1]);
+            float m = rm[t];
 #pragma unroll
-            for (int i = 2; i < 16; ++i) m = fmaxf(m, acc[t][i]);
-            rm[t] = fmaxf(rm[t], m);
+            for (int i = 0; i < 16; i += 2) m = fmaxf(fmaxf(m, acc[t][i]), acc[t][i + 1]);
+            rm[t] = m;
         }
     };
 
@@ -158,17 +168,21 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, Prefill
     __syncthreads();
     for (int c = c_begin; c < c_end; ++c) {
         const int buf = (c - c_begin) & 1;
-        if (c + 1 < c_end) load_chunk(c + 1);   // in flight while this chunk is multiplied
+        // The next chunk's loads are in flight while this chunk is multiplied.
+        // They are issued on every iteration (the last one reloads its own
+        // chunk) so that the newest loads are always queries: waiting for the
+        // key operands then never waits for them.
+        load_chunk(c + 1 < c_end ? c + 1 : c);
         if (active) {
 #pragma unroll
             for (int qt = 0; qt < kChunk / 32; ++qt) tile(buf, qt);
         }
-        if (c + 1 < c_end) store_chunk(buf ^ 1);   // that buffer was last read before the previous barrier
+        store_chunk(buf ^ 1);   // that buffer was last read before the previous barrier
         __syncthreads();
     }
     if (!active) return;
 
-    uint32_t* out = keys + ((int64_t)l * a.S + s) * a.n;
+    uint32_t* out = bits + ((int64_t)l * a.S + s) * a.n;
     const int fill_s = fill_of(a, s);   // tokens of the last block that are scored
     if (a.fill && grp == 0 && kv == 0 && part == 0 && l == 0 && tid == 0 && (a.fill[s] < 0 || a.fill[s] > BS))
         atomicOr(a.err, DEVERR_FILL);
@@ -186,8 +200,12 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, Prefill
         if constexpr (BS >= 32) v = fmaxf(v, lane_xor<16>(v));
         const int64_t key = key0 + t * 32 + col;
         if (half == 0 && (col % BS) == 0 && key < gm.n_keys) {
-            if ((live >> t) & 1u) atomicMax(out + key / BS, order_key(v));
-            else if (kv == 0 && part == 0) atomicOr(a.err, DEVERR_TABLE);
+            if ((live >> t) & 1u) {
+                atomic_max_bits(out + key / BS, v);
+            } else if (kv == 0 && part == 0) {
+                atomicMax(reinterpret_cast<int*>(out + key / BS), 0x7FC00000);   // NaN: above every number's bits
+                atomicOr(a.err, DEVERR_TABLE);
+            }
         }
     }
 }
@@ -195,12 +213,6 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, Prefill
 __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = v;
-}
-
-// Keys back to float32 in place; a block no workgroup wrote (invalid table entry) becomes NaN.
-__global__ __launch_bounds__(256) void keys_to_scores_kernel(uint32_t* p, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) reinterpret_cast<float*>(p)[i] = key_to_float(p[i]);
 }
 
 template <int R, int NKT, int BS>
@@ -253,14 +265,13 @@ hipError_t launch_score_prefill(const ScoreArgs& a, hipStream_t st) {
     if (!grid_fits(gm.groups * gm.q_split * a.Hk * a.S * a.n_layers) || !grid_fits((total + 255) / 256))
         return hipErrorInvalidConfiguration;
     const unsigned fill_grid = (unsigned)((total + 255) / 256);
-    fill_u32_kernel<<<fill_grid, 256, 0, st>>>(keys, total, 0u);
+    fill_u32_kernel<<<fill_grid, 256, 0, st>>>(keys, total, 0xFF800000u);   // -inf
     switch (a.R) {
         case 16: launch_bs<16, nkt_for(16)>(a, gm, keys, st); break;
         case 32: launch_bs<32, nkt_for(32)>(a, gm, keys, st); break;
         case 64: launch_bs<64, nkt_for(64)>(a, gm, keys, st); break;
         default: launch_bs<128, nkt_for(128)>(a, gm, keys, st); break;
     }
-    keys_to_scores_kernel<<<fill_grid, 256, 0, st>>>(keys, total);
     return hipGetLastError();
 }
 

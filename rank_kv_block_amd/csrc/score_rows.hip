@@ -9,70 +9,65 @@
 // complete(r) <= b < stride.  A complete block whose table entry is outside
 // [0, max_blocks) scores NaN and raises the device error word.
 //
-// Per row tile of 32 rows the contraction is A_kv(h) [32 keys, R] x Q_h^T [R,
-// 32 rows] for every query head h, on v_mfma_f32_32x32x16_bf16 with f32
-// accumulation (keys as the A operand, so a lane holds one query row and 16
-// keys of the tile: element i is key (i / 4) * 8 + 4 * (lane / 32) + i % 4).
-// The four waves of a workgroup share one range of NKT tiles of 32 keys
-// (consecutive tokens of consecutive blocks) and split the query heads: wave w
-// takes heads [w * Hq / 4, (w + 1) * Hq / 4), whose one or two kv heads' keys
-// it keeps in registers.  Each query operand read from LDS then serves NKT
-// tiles.  After every head a lane folds its 16 products into the running
-// maxima of the tile's blocks (B / 2 elements per block, max3 chains); after a
-// row tile the two lane halves are combined, the four waves' partial maxima
-// meet in LDS and the workgroup writes each row's blocks with stores that run
-// along the row.
+// Work split.  A workgroup has 8 waves; wave w serves kv head w % Hk and, when
+// there are fewer than 8 kv heads, the (w / Hk)-th of 8 / Hk key sub-ranges.
+// A key group is the workgroup's keys: 8 / Hk sub-ranges of KT tiles of 32
+// keys (consecutive tokens of consecutive blocks).  A wave keeps its keys of
+// its kv head as MFMA A operands in registers and, per row tile of 32 rows,
+// multiplies them by the queries of that kv head's g query heads, one head per
+// step: A_kv [32 keys, R] x Q_h^T [R, 32 rows] on v_mfma_f32_32x32x16_bf16 (f32
+// accumulation; a lane holds one query row and 16 keys of a tile: element i is
+// key (i / 4) * 8 + 4 * (lane / 32) + i % 4), and folds each product into the
+// running maxima of the tile's blocks.
 //
-// Query vectors stream through LDS in stages of 32 rows x (4 waves x SH heads),
-// double-buffered: all 256 threads load the next stage with 16-byte reads while
-// the current one is multiplied, and each wave reads its own heads' vectors in
-// the MFMA layout (vectors padded by 16 bytes so the rows of one read fall in
-// distinct banks).
+// Each wave streams its own queries: per step it loads the next step's 32
+// query vectors with 16-byte coalesced reads into registers, multiplies the
+// current step's vectors from its private LDS buffer (padded rows, so the MFMA
+// operand reads are free of bank conflicts), then writes the next step's
+// vectors to its other private buffer.  No query stage is shared, so the waves
+// never wait for each other inside a row tile.  They meet once per row tile:
+// each wave's block maxima (lane halves combined) go to LDS, one barrier, and
+// the workgroup takes the max over kv heads and stores the row tile's scores
+// along rows.  The reduction buffer is double-buffered where LDS allows, so
+// that barrier is the only one.
 //
-// Causality: key tiles that start at or past the last row's complete blocks
-// skip their MFMAs (their scores are all -inf); tiles are in key order, so the
-// ones still needed are a prefix, the same for every wave.
-//
-// A workgroup holds PRED_ROWS_KG key groups of four waves that share each query
-// stage.  Workgroups are (key range) x (row part) with the row part fastest:
-// with 4 or 8 parts every XCD (each takes every 8th workgroup) serves one or
-// two parts, and its L2 holds only those parts' queries.
+// Scheduling.  One workgroup per CU (two waves per SIMD), as many as the GPU
+// has CUs.  The rows are cut into up to 8 parts; workgroup i serves part
+// i % parts, so with 8 parts each XCD (which takes every 8th workgroup) serves
+// one part and its L2 holds that part's queries.  A part's work items --
+// (key group, row tile), key group major -- are split into equal contiguous
+// ranges over its workgroups; a wave reloads its keys only when the group
+// changes, and issues that load before the previous item's reduction so the
+// reduction hides part of its latency.  Key tiles past the row tile's last
+// complete block skip their MFMAs (their scores are -inf).
 #include "common.h"
 #include "kernels.h"
 
-// Tuning knobs (compile-time), each measured on the 2048-row prefill chunk
-// (r = 64, 8 kv heads): 96 key registers (3 tiles) keep two waves per SIMD
-// (128 registers: 4 tiles, one wave, 580 us; 96: 455 us); 8192 target waves
-// give 8 row parts there, so an XCD's L2 holds one part's 1 MiB of queries
-// (444 us); two key groups per workgroup share each query stage, halving the
-// query reads (427-440 us).  Two-head stages at r = 64 measured no better.
-#ifndef PRED_ROWS_TARGET_WAVES
-#define PRED_ROWS_TARGET_WAVES 8192
+// Tuning knobs (compile-time).
+// key registers per wave: KT = PRED_ROWS_KEY_REGS / (4 * R / 16) tiles, at most 8
+#ifndef PRED_ROWS_KEY_REGS
+#define PRED_ROWS_KEY_REGS 96
 #endif
-// key groups per workgroup: KG groups of four waves share each query stage
-#ifndef PRED_ROWS_KG
-#define PRED_ROWS_KG 2
-#endif
-// stages of two heads per wave for r up to this (one head above)
-#ifndef PRED_ROWS_SH2_MAX_R
-#define PRED_ROWS_SH2_MAX_R 32
+// row parts (an XCD's L2 holds one part's queries when there are 8)
+#ifndef PRED_ROWS_MAX_PARTS
+#define PRED_ROWS_MAX_PARTS 8
 #endif
 
 namespace pred {
 
 namespace {
 
-constexpr int kWaves = 4;                         // waves of one key group (they split the heads)
-constexpr int kKG = PRED_ROWS_KG;
-constexpr int kThreads = 256 * kKG;
-constexpr int64_t kTargetWaves = PRED_ROWS_TARGET_WAVES;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kLdsBytes = 160 * 1024;
 
 struct RowGeom {
-    int64_t groups;       // workgroups along the keys (kKG * NKT * 32 keys each)
+    int wpk;              // waves per kv head: 8 / Hk key sub-ranges
+    int64_t groups;       // key groups (wpk * KT * 32 keys each)
     int row_tiles;        // ceil(rows / 32)
     int parts;            // row parts
     int tiles_per_part;
-    int stages;           // stages per row tile: (Hq / 4) / SH
+    int wg_per_part;      // workgroups serving each part
 };
 
 __device__ inline int64_t complete_blocks(const RowScoreArgs& a, int64_t r) {
@@ -80,191 +75,268 @@ __device__ inline int64_t complete_blocks(const RowScoreArgs& a, int64_t r) {
     return c < a.n ? c : a.n;
 }
 
-// R: projected width; KPW: kv heads per wave (2 when Hk = 8, else 1); NKT:
-// 32-key tiles per wave; SH: heads per wave per stage; BS: block size.
-template <int R, int KPW, int NKT, int SH, int BS>
+constexpr int kt_rows(int r) {
+    const int t = (PRED_ROWS_KEY_REGS / 4) / (r / 16);
+    return t < 1 ? 1 : (t > 8 ? 8 : t);
+}
+
+template <int R, int BS>
+struct RowsLds {
+    static constexpr int KT = kt_rows(R);
+    static constexpr int ROWB = R * 2 + 16;                    // LDS bytes per query vector
+    static constexpr int BPT = 32 / BS;                        // blocks per key tile
+    static constexpr int NB = KT * BPT;                        // blocks of a wave's keys
+    static constexpr int NBP = NB | 1;                         // reduction row stride (odd: no bank conflicts)
+    static constexpr int STAGE = 32 * ROWB;                    // one head of one row tile
+    static constexpr int RED = kWaves * 32 * NBP * 4;          // one reduction buffer
+    static constexpr int NRED = (kWaves * 2 * STAGE + 2 * RED <= kLdsBytes) ? 2 : 1;
+    static_assert(kWaves * 2 * STAGE + RED <= kLdsBytes, "query stages and reduction exceed LDS");
+};
+
+// R: projected width; BS: block size.
+template <int R, int BS>
 __global__ __launch_bounds__(kThreads) void score_rows_kernel(RowScoreArgs a, RowGeom gm) {
+    using L = RowsLds<R, BS>;
+    constexpr int KT = L::KT;
     constexpr int RS = R / 16;                        // MFMA k-steps of 16
     constexpr int CPR = R / 8;                        // 16-byte pieces per query vector
-    constexpr int ROWB = R * 2 + 16;                  // LDS bytes per query vector
-    constexpr int VEC = 32 * kWaves * SH;             // query vectors per stage
-    constexpr int PIECES = VEC * CPR;                 // 16-byte pieces per stage
-    constexpr int PPT = (PIECES + kThreads - 1) / kThreads;   // pieces per thread
-    constexpr bool kFull = PIECES % kThreads == 0;            // every thread has PPT pieces
-    constexpr int BPT = 32 / BS;                      // blocks per key tile
+    constexpr int ROWB = L::ROWB;
+    constexpr int PPL = (32 * CPR) / 64;              // pieces per lane per step (>= 1 for R >= 16)
+    constexpr int BPT = L::BPT;
     constexpr int EPB = BS / 2;                       // accumulator elements per block in a lane
-    constexpr int NB = NKT * BPT;                     // blocks of a key group
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2][VEC * ROWB];
-    __shared__ float red[kKG][kWaves][NB * 32];       // partial maxima [key group][wave][block][row]
+    constexpr int NB = L::NB;
+    constexpr int NRED = L::NRED;
+    __shared__ __attribute__((aligned(16))) unsigned char stage[kWaves][2][L::STAGE];
+    constexpr int NBP = L::NBP;
+    __shared__ float red[NRED][kWaves][32 * NBP];     // per wave: block maxima [row][block]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = (tid >> 6) % kWaves;             // head quarter
-    const int kg = (tid >> 6) / kWaves;               // key group of this wave
-    const int part = (int)(blockIdx.x % gm.parts);
-    const int64_t grp = blockIdx.x / gm.parts;
-    const int rt_begin = part * gm.tiles_per_part;
-    const int rt_end = (rt_begin + gm.tiles_per_part) < gm.row_tiles ? (rt_begin + gm.tiles_per_part) : gm.row_tiles;
-    if (rt_begin >= rt_end) return;   // whole workgroup
-    const int qh = a.Hq / kWaves;     // heads per wave
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kv = w % a.Hk;
+    const int sub = w / a.Hk;
     const int g = a.Hq / a.Hk;
-    const int kv_first = (wave * qh) / g;
-    const int col = lane & 31;        // key of a tile (A operand) / query row (B operand)
-    const int half = lane >> 5;       // which 8 of the 16 k-values of one MFMA step
+    const int part = (int)(blockIdx.x % gm.parts);
+    const int jw = (int)(blockIdx.x / gm.parts);
+    const int t_first = part * gm.tiles_per_part;
+    const int nt = (gm.row_tiles - t_first) < gm.tiles_per_part ? (gm.row_tiles - t_first) : gm.tiles_per_part;
+    if (nt <= 0) return;   // whole workgroup
+    const int64_t items = gm.groups * nt;
+    const int64_t i_begin = items * jw / gm.wg_per_part;
+    const int64_t i_end = items * (jw + 1) / gm.wg_per_part;
+    if (i_begin >= i_end) return;   // whole workgroup
+    const int col = lane & 31;      // key of a tile (A operand) / query row (B operand)
+    const int half = lane >> 5;     // which 8 of the 16 k-values of one MFMA step
     const int64_t n_keys = a.n * BS;
-    const int64_t key0 = (grp * kKG + kg) * (NKT * 32);
     const int64_t slot_elems = (int64_t)a.Hk * BS * R;
+    const uint32_t row_bytes = (uint32_t)a.Hq * R * 2;   // one query row, all heads
+    const uint32_t my_lds = (uint32_t)(uintptr_t)&stage[w][0][0];
 
-    // A operands: this lane's key of every tile, for the wave's kv heads.
-    bf16x8_t kb[NKT][KPW][RS];
+    // Per-lane constants of a step: piece i of the lane is query row p / CPR of
+    // the tile, 16-byte piece p % CPR (p = lane + 64 i): its byte offset from the
+    // tile's head-0 vector of row 0, and its LDS offset in a stage buffer.
+    uint32_t q_off[PPL], l_off[PPL];
 #pragma unroll
-    for (int t = 0; t < NKT; ++t) {
-        const int64_t key = key0 + t * 32 + col;
-        const uint16_t* src = a.ag;   // in bounds for lanes without a valid key; their blocks are never stored
-        if (key < n_keys) {
-            const int64_t b = key / BS;
-            const int tok = (int)(key - b * BS);
-            const int64_t phys = a.table ? (int64_t)a.table[b] : b;
-            if (phys >= 0 && phys < a.N) src = a.ag + (a.layer * a.N + phys) * slot_elems + (int64_t)tok * R;
-        }
-#pragma unroll
-        for (int k = 0; k < KPW; ++k) {
-            const int kv = (kv_first + k) < a.Hk ? kv_first + k : a.Hk - 1;
-#pragma unroll
-            for (int st = 0; st < RS; ++st) kb[t][k][st] = load8(src + (int64_t)kv * BS * R + st * 16 + half * 8);
-        }
+    for (int i = 0; i < PPL; ++i) {
+        const int p = lane + 64 * i;
+        q_off[i] = (uint32_t)(p / CPR) * row_bytes + (uint32_t)(p % CPR) * 16;
+        l_off[i] = (uint32_t)((p / CPR) * ROWB + (p % CPR) * 16);
     }
+    const uint32_t rd_off = (uint32_t)(col * ROWB + half * 16);   // MFMA operand read, k-step 0
 
-    float rm[NKT][BPT];
+    // A operands: this lane's key of each of the wave's tiles in group grp
+    bf16x8_t kb[KT][RS];
+    auto load_keys = [&](int64_t grp) {
 #pragma unroll
-    for (int t = 0; t < NKT; ++t)
+        for (int t = 0; t < KT; ++t) {
+            const int64_t key = (grp * gm.wpk + sub) * (KT * 32) + t * 32 + col;
+            const uint16_t* src = a.ag;   // lanes without a valid key: in bounds; their blocks are never stored
+            if (key < n_keys) {
+                const int64_t b = key / BS;
+                const int tok = (int)(key - b * BS);
+                const int64_t phys = a.table ? (int64_t)a.table[b] : b;
+                if (phys >= 0 && phys < a.N)
+                    src = a.ag + (a.layer * a.N + phys) * slot_elems + ((int64_t)kv * BS + tok) * R;
+            }
+#pragma unroll
+            for (int st = 0; st < RS; ++st) kb[t][st] = load8(src + st * 16 + half * 8);
+        }
+    };
+
+    float rm[KT][BPT];
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
 #pragma unroll
         for (int bi = 0; bi < BPT; ++bi) rm[t][bi] = -__builtin_inff();
 
-    // stage (row tile rt, stage s): vector v = row * (4 SH) + slot, slot = wave * SH + j,
-    // holding head wave * qh + s * SH + j of that row; LDS keeps it at slot * 32 + row
-    u32x4_t gq[PPT];
-    auto piece_src = [&](int rt, int s, int p) -> const u32x4_t* {
-        const int v = p / CPR;
-        const int slot = v % (kWaves * SH);
-        int64_t r = (int64_t)rt * 32 + v / (kWaves * SH);
-        if (r >= a.rows) r = a.rows - 1;   // padding rows repeat a real row
-        const int h = (slot / SH) * qh + s * SH + slot % SH;
-        return reinterpret_cast<const u32x4_t*>(a.qp + (r * a.Hq + h) * R + (p % CPR) * 8);
+    // query vectors of one step (row tile rt, head h) -> registers: buffer loads
+    // from the tile's first row, whose range ends at the last real row, so the
+    // padding rows of a partial tile read zeros (never stored)
+    u32x4_t gq[PPL];
+    auto fetch = [&](int rt, int h) {
+        const int64_t r0 = (int64_t)rt * 32;
+        const int64_t left = a.rows - r0 < 32 ? a.rows - r0 : 32;
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(a.qp + r0 * a.Hq * R), (short)0, (int)((uint32_t)left * row_bytes), 0x00020000);
+        const int soff = h * R * 2;
+#pragma unroll
+        for (int i = 0; i < PPL; ++i)
+            gq[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)q_off[i], soff, 0));
     };
-    auto piece_dst = [&](int buf, int p) -> u32x4_t* {
-        const int v = p / CPR;
-        const int vec = (v % (kWaves * SH)) * 32 + v / (kWaves * SH);
-        return reinterpret_cast<u32x4_t*>(&lds[buf][vec * ROWB + (p % CPR) * 16]);
+    auto put = [&](int buf) {
+        const uint32_t base = my_lds + (uint32_t)(buf * L::STAGE);
+#pragma unroll
+        for (int i = 0; i < PPL; ++i)
+            *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(base + l_off[i]) = gq[i];
     };
-    // this wave's heads of stage s against its first ntl key tiles
-    auto stage_mfma = [&](int buf, int s, int ntl) {
+    auto chain = [&](int t, const bf16x8_t (&qb)[RS]) {
+        f32x16_t acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[t][0], qb[0], f32x16_t{}, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < SH; ++j) {
-            const int h = wave * qh + s * SH + j;
-            const int lk = h / g - kv_first;   // which of the wave's kv heads (wave-uniform)
-            bf16x8_t qb[RS];
+        for (int st = 1; st < RS; ++st) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[t][st], qb[st], acc, 0, 0, 0);
+        return acc;
+    };
+    auto fold = [&](int t, const f32x16_t& acc) {
 #pragma unroll
-            for (int st = 0; st < RS; ++st)
-                qb[st] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                        &lds[buf][((wave * SH + j) * 32 + col) * ROWB + (st * 2 + half) * 16]));
+        for (int bi = 0; bi < BPT; ++bi) {
+            float m = rm[t][bi];
 #pragma unroll
-            for (int k = 0; k < KPW; ++k) {
-                if (KPW > 1 && k != lk) continue;
-                // each tile's chain, then its fold: the fold of tile t overlaps the
-                // chain of tile t + 1, and only two accumulators are live
-#pragma unroll
-                for (int t = 0; t < NKT; ++t) {
-                    if (t < ntl) {
-                        f32x16_t acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[t][k][0], qb[0], f32x16_t{}, 0, 0, 0);
-#pragma unroll
-                        for (int st = 1; st < RS; ++st)
-                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[t][k][st], qb[st], acc, 0, 0, 0);
-#pragma unroll
-                        for (int bi = 0; bi < BPT; ++bi) {
-                            float m = rm[t][bi];
-#pragma unroll
-                            for (int e = 0; e < EPB; e += 2) m = fmaxf(m, fmaxf(acc[bi * EPB + e], acc[bi * EPB + e + 1]));
-                            rm[t][bi] = m;
-                        }
-                    }
-                }
-            }
+            for (int e = 0; e < EPB; e += 2) m = fmaxf(fmaxf(m, acc[bi * EPB + e]), acc[bi * EPB + e + 1]);
+            rm[t][bi] = m;
         }
     };
-    // row tile rt done: combine the lane halves and the waves, store, reset
-    auto epilogue = [&](int rt) {
+    // The wave's first ntl key tiles against the vectors in buffer buf.  With
+    // every tile live, tile t + 1's chain is issued before tile t's fold, so the
+    // fold's VALU work runs while the matrix core multiplies.
+    auto multiply = [&](int buf, int ntl) {
+        const uint32_t base = my_lds + (uint32_t)(buf * L::STAGE) + rd_off;
+        bf16x8_t qb[RS];
 #pragma unroll
-        for (int t = 0; t < NKT; ++t)
+        for (int st = 0; st < RS; ++st)
+            qb[st] = __builtin_bit_cast(bf16x8_t,
+                                        *reinterpret_cast<__attribute__((address_space(3))) const u32x4_t*>(base + st * 32));
+        if (ntl == KT) {
+            f32x16_t acc[2];
+            acc[0] = chain(0, qb);
 #pragma unroll
-            for (int bi = 0; bi < BPT; ++bi) {
-                const float v = fmaxf(rm[t][bi], lane_xor<32>(rm[t][bi]));
-                if (half == 0) red[kg][wave][(t * BPT + bi) * 32 + col] = v;
-                rm[t][bi] = -__builtin_inff();
+            for (int t = 1; t < KT; ++t) {
+                acc[t & 1] = chain(t, qb);
+                fold(t - 1, acc[(t - 1) & 1]);
             }
-        __syncthreads();
-        const int64_t r0 = (int64_t)rt * 32;
-        const int64_t blk0 = grp * kKG * NB;          // first block of the workgroup
-        for (int i = tid; i < kKG * NB * 32; i += kThreads) {
-            const int row = i / (kKG * NB);           // consecutive threads: consecutive blocks of a row
-            const int bw = i - row * (kKG * NB);
-            const int g2 = bw / NB;
-            const int blk = bw - g2 * NB;
+            fold(KT - 1, acc[(KT - 1) & 1]);
+            return;
+        }
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+            if (t < ntl) fold(t, chain(t, qb));
+    };
+
+    // Stores of one row tile: entry i = tid + 512 j of the 32 x nbg (row, block)
+    // maxima, consecutive threads on consecutive blocks of a row; the max over
+    // the kv heads' partial maxima, -inf for an incomplete block, NaN for an
+    // invalid table entry.
+    const int nbg = gm.wpk * NB;   // blocks of a group
+    auto store_tile = [&](int rb, int64_t sgrp, int srt) {
+        const int64_t r0 = (int64_t)srt * 32;
+        const int64_t blk0 = sgrp * nbg;
+        for (int i = tid; i < nbg * 32; i += kThreads) {
+            const int row = i / nbg;
+            const int bw = i - row * nbg;
+            const int s2 = bw / NB;
+            const int blk = bw - s2 * NB;
             const int64_t r = r0 + row;
             const int64_t b = blk0 + bw;
             if (r < a.rows && b < a.n) {
-                float v = fmaxf(fmaxf(red[g2][0][blk * 32 + row], red[g2][1][blk * 32 + row]),
-                                fmaxf(red[g2][2][blk * 32 + row], red[g2][3][blk * 32 + row]));
-                if (b >= complete_blocks(a, r)) {
-                    v = -__builtin_inff();
-                } else if (a.table) {
-                    const int64_t phys = a.table[b];
-                    if (phys < 0 || phys >= a.N) {
-                        v = __uint_as_float(0x7FC00000u);
-                        atomicOr(a.err, DEVERR_TABLE);
-                    }
+                const bool complete = b < (a.first_pos + r + 1) / BS;
+                const int64_t phys = (complete && a.table) ? (int64_t)a.table[b] : 0;   // in flight during the reads
+                // the kv heads' partial maxima: all reads issued before the first is needed
+                const float* src = &red[rb][s2 * a.Hk][row * NBP + blk];
+                float part[kWaves];
+#pragma unroll
+                for (int k = 0; k < kWaves; ++k) part[k] = k < a.Hk ? src[k * 32 * NBP] : -__builtin_inff();
+                float v = part[0];
+#pragma unroll
+                for (int k = 1; k < kWaves; ++k) v = fmaxf(v, part[k]);
+                uint32_t bits = __float_as_uint(v);
+                if (!complete) {
+                    bits = 0xFF800000u;   // -inf
+                } else if (phys < 0 || phys >= a.N) {
+                    bits = 0x7FC00000u;   // NaN (as bits: this file is compiled without NaN semantics)
+                    atomicOr(a.err, DEVERR_TABLE);
                 }
-                a.scores[r * a.stride + b] = v;
+                reinterpret_cast<uint32_t*>(a.scores)[r * a.stride + b] = bits;
             }
         }
-        // red is written again only after the next row tile's stage barriers
     };
 
+    int64_t grp = i_begin / nt;
+    int rt = t_first + (int)(i_begin - grp * nt);
     int buf = 0;
-#pragma unroll
-    for (int i = 0; i < PPT; ++i)
-        if (kFull || tid + kThreads * i < PIECES) gq[i] = *piece_src(rt_begin, 0, tid + kThreads * i);
-#pragma unroll
-    for (int i = 0; i < PPT; ++i)
-        if (kFull || tid + kThreads * i < PIECES) *piece_dst(0, tid + kThreads * i) = gq[i];
-    __syncthreads();
-    for (int rt = rt_begin; rt < rt_end; ++rt) {
-        // key tiles that hold a block complete for the tile's last row
+    int red_buf = 0;
+    // the previous row tile, stored during this one's first step (two reduction buffers)
+    bool pending = false;
+    int64_t p_grp = 0;
+    int p_rt = 0;
+    load_keys(grp);
+    fetch(rt, kv * g);
+    put(0);
+    for (int64_t item = i_begin; item < i_end; ++item) {
+        const bool more = item + 1 < i_end;
+        const int n_rt = (rt + 1 - t_first) < nt ? rt + 1 : t_first;
+        const int64_t n_grp = n_rt == t_first ? grp + 1 : grp;
+        // key tiles holding a block complete for the row tile's last row
         const int64_t last = ((int64_t)rt * 32 + 31) < a.rows ? ((int64_t)rt * 32 + 31) : a.rows - 1;
-        const int64_t climit = complete_blocks(a, last);
+        int64_t climit = (a.first_pos + last + 1) / BS;
+        if (climit > a.n) climit = a.n;
+        const int64_t key_first = (grp * gm.wpk + sub) * (KT * 32);
         int ntl = 0;
 #pragma unroll
-        for (int t = 0; t < NKT; ++t)
-            if ((key0 + t * 32) / BS < climit) ntl = t + 1;
-        for (int s = 0; s < gm.stages; ++s) {
-            const bool last_stage = s + 1 == gm.stages;
-            const int nrt = last_stage ? rt + 1 : rt;   // the next stage
-            const int ns = last_stage ? 0 : s + 1;
-            const bool more = nrt < rt_end;
-            if (more)   // in flight while this stage is multiplied
-#pragma unroll
-                for (int i = 0; i < PPT; ++i)
-                    if (kFull || tid + kThreads * i < PIECES) gq[i] = *piece_src(nrt, ns, tid + kThreads * i);
-            if (ntl > 0) stage_mfma(buf, s, ntl);
-            if (more)   // that buffer was last read before the previous barrier
-#pragma unroll
-                for (int i = 0; i < PPT; ++i)
-                    if (kFull || tid + kThreads * i < PIECES) *piece_dst(buf ^ 1, tid + kThreads * i) = gq[i];
-            __syncthreads();
+        for (int t = 0; t < KT; ++t)
+            if ((key_first + t * 32) / BS < climit) ntl = t + 1;
+        for (int hs = 0; hs < g; ++hs) {
+            // The next step's vectors are in flight during this step's MFMAs.  The
+            // fetch is unconditional (the last step re-reads its own vectors) so
+            // that on every path the newest loads are queries, and waiting for the
+            // keys never waits for them.
+            const bool last_step = hs + 1 == g;
+            fetch(last_step ? (more ? n_rt : rt) : rt, kv * g + (last_step ? (more ? 0 : hs) : hs + 1));
+            multiply(buf, ntl);
+            if (NRED == 2 && hs == 0 && pending) {
+                // the previous row tile's stores, while this step's MFMAs run
+                store_tile(red_buf ^ 1, p_grp, p_rt);
+                pending = false;
+            }
+            put(buf ^ 1);   // that buffer's vectors were read by the previous step
             buf ^= 1;
         }
-        epilogue(rt);
+        // row tile done: the next group's keys first (their latency overlaps the reduction)
+        if (more && n_grp != grp) load_keys(n_grp);
+        float* rw = &red[red_buf][w][0];
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int bi = 0; bi < BPT; ++bi) {
+                // rows 0..15 and 16..31 of each key sit in the two lane halves
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rm[t][bi]),
+                                                                 __float_as_uint(rm[t][bi]), false, false);
+                if (half == 0) rw[col * NBP + t * BPT + bi] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                rm[t][bi] = -__builtin_inff();
+            }
+        // every wave's maxima of this row tile are in LDS; every wave has also
+        // finished the previous row tile's stores, so its buffer is free again
+        __syncthreads();
+        if constexpr (NRED == 2) {
+            pending = true;
+            p_grp = grp;
+            p_rt = rt;
+            red_buf ^= 1;
+        } else {
+            store_tile(0, grp, rt);
+            __syncthreads();   // the buffer is written again next row tile
+        }
+        grp = n_grp;
+        rt = n_rt;
     }
+    if (pending) store_tile(red_buf ^ 1, p_grp, p_rt);
 }
 
 // Any shape: one thread per (row, column of the stride), f32 dot products.
@@ -280,7 +352,7 @@ __global__ __launch_bounds__(256) void score_rows_generic_kernel(RowScoreArgs a)
     }
     const int64_t phys = a.table ? (int64_t)a.table[b] : b;
     if (phys < 0 || phys >= a.N) {
-        *out = __uint_as_float(0x7FC00000u);
+        *reinterpret_cast<uint32_t*>(out) = 0x7FC00000u;   // NaN (as bits: no NaN semantics in this file)
         atomicOr(a.err, DEVERR_TABLE);
         return;
     }
@@ -310,59 +382,36 @@ __global__ __launch_bounds__(256) void fill_tail_cols_kernel(float* scores, int6
     scores[r * stride + n + (i - r * w)] = -__builtin_inff();
 }
 
-// 32-key tiles per wave: the keys take NKT * KPW * R / 4 registers, kept at
-// PRED_ROWS_KEY_REGS
-#ifndef PRED_ROWS_KEY_REGS
-#define PRED_ROWS_KEY_REGS 96
-#endif
-constexpr int nkt_rows(int r, int kpw) {
-    const int t = (PRED_ROWS_KEY_REGS / 4) / (kpw * (r / 16));
-    return t < 1 ? 1 : (t > 4 ? 4 : t);
-}
-
-template <int R, int KPW, int BS>
+template <int R, int BS>
 hipError_t launch_rk(const RowScoreArgs& a, hipStream_t st) {
-    constexpr int NKT = nkt_rows(R, KPW);
-    const int qh = a.Hq / kWaves;
-    const int sh = (R <= PRED_ROWS_SH2_MAX_R && qh % 2 == 0) ? 2 : 1;
+    constexpr int KT = RowsLds<R, BS>::KT;
     RowGeom gm;
+    gm.wpk = kWaves / a.Hk;
     const int64_t n_keys = a.n * BS;
-    gm.groups = (n_keys + kKG * NKT * 32 - 1) / (kKG * NKT * 32);
+    const int64_t keys_per_group = (int64_t)gm.wpk * KT * 32;
+    gm.groups = (n_keys + keys_per_group - 1) / keys_per_group;
     gm.row_tiles = (int)((a.rows + 31) / 32);
-    gm.stages = qh / sh;
-    int64_t parts = (kTargetWaves + gm.groups * kWaves * kKG - 1) / (gm.groups * kWaves * kKG);
-    if (parts > gm.row_tiles) parts = gm.row_tiles;
-    if (parts < 1) parts = 1;
-    gm.tiles_per_part = (int)((gm.row_tiles + parts - 1) / parts);
+    int parts = PRED_ROWS_MAX_PARTS;
+    while (parts > 1 && parts > gm.row_tiles) parts >>= 1;
+    gm.tiles_per_part = (gm.row_tiles + parts - 1) / parts;
     gm.parts = (gm.row_tiles + gm.tiles_per_part - 1) / gm.tiles_per_part;   // no empty parts
-    const int64_t wgs = gm.groups * gm.parts;
+    const int64_t items_per_part = gm.groups * gm.tiles_per_part;
+    int64_t wpp = (a.n_cu > 0 ? a.n_cu : 256) / gm.parts;
+    if (wpp < 1) wpp = 1;
+    if (wpp > items_per_part) wpp = items_per_part;
+    gm.wg_per_part = (int)wpp;
+    const int64_t wgs = (int64_t)gm.parts * wpp;
     if (!grid_fits(wgs)) return hipErrorInvalidConfiguration;
-    if constexpr (R <= PRED_ROWS_SH2_MAX_R) {
-        if (sh == 2) {
-            score_rows_kernel<R, KPW, NKT, 2, BS><<<(unsigned)wgs, kThreads, 0, st>>>(a, gm);
-            return hipGetLastError();
-        }
-    }
-    score_rows_kernel<R, KPW, NKT, 1, BS><<<(unsigned)wgs, kThreads, 0, st>>>(a, gm);
+    score_rows_kernel<R, BS><<<(unsigned)wgs, kThreads, 0, st>>>(a, gm);
     return hipGetLastError();
 }
 
-template <int R, int KPW>
+template <int R>
 hipError_t launch_rb(const RowScoreArgs& a, hipStream_t st) {
     switch (a.B) {
-        case 8: return launch_rk<R, KPW, 8>(a, st);
-        case 16: return launch_rk<R, KPW, 16>(a, st);
-        default: return launch_rk<R, KPW, 32>(a, st);
-    }
-}
-
-template <int KPW>
-hipError_t launch_kpw(const RowScoreArgs& a, hipStream_t st) {
-    switch (a.R) {
-        case 16: return launch_rb<16, KPW>(a, st);
-        case 32: return launch_rb<32, KPW>(a, st);
-        case 64: return launch_rb<64, KPW>(a, st);
-        default: return launch_rb<128, KPW>(a, st);
+        case 8: return launch_rk<R, 8>(a, st);
+        case 16: return launch_rk<R, 16>(a, st);
+        default: return launch_rk<R, 32>(a, st);
     }
 }
 
@@ -370,7 +419,7 @@ bool rows_mfma_supported(const RowScoreArgs& a) {
     const bool r_ok = a.R == 16 || a.R == 32 || a.R == 64 || a.R == 128;
     const bool hk_ok = a.Hk == 1 || a.Hk == 2 || a.Hk == 4 || a.Hk == 8;
     const bool b_ok = a.B == 8 || a.B == 16 || a.B == 32;
-    return r_ok && hk_ok && b_ok && a.Hq % kWaves == 0;
+    return r_ok && hk_ok && b_ok;
 }
 
 }  // namespace
@@ -391,7 +440,13 @@ hipError_t launch_score_rows(const RowScoreArgs& a, int force, hipStream_t st) {
     m.n = n_cols;
     const int64_t tail = a.rows * (a.stride - n_cols);
     if (!grid_fits((tail + 255) / 256)) return hipErrorInvalidConfiguration;
-    const hipError_t e = a.Hk == 8 ? launch_kpw<2>(m, st) : launch_kpw<1>(m, st);
+    hipError_t e;
+    switch (a.R) {
+        case 16: e = launch_rb<16>(m, st); break;
+        case 32: e = launch_rb<32>(m, st); break;
+        case 64: e = launch_rb<64>(m, st); break;
+        default: e = launch_rb<128>(m, st); break;
+    }
     if (e != hipSuccess || tail == 0) return e;
     fill_tail_cols_kernel<<<(unsigned)((tail + 255) / 256), 256, 0, st>>>(a.scores, a.rows, a.stride, n_cols);
     return hipGetLastError();
