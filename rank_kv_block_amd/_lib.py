@@ -7,7 +7,9 @@ fallback implementation behind these names.
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpred.so")
+# PRED_LIBRARY selects another build of the same library (e.g. the host-side
+# sanitizer build the CPU tests load); by default the in-tree libpred.so.
+LIB_PATH = os.environ.get("PRED_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpred.so")
 
 PRED_OK = 0
 PRED_ERR_INVALID_DIMS = -1

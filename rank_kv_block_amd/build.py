@@ -62,6 +62,65 @@ def build(verbose=False):
     return LIB
 
 
+# Host-side sanitizer build: the same library with AddressSanitizer and
+# UndefinedBehaviorSanitizer on its host code (argument checks, sizing, the
+# projection generator, launch set-up), for the CPU tests of the C ABI.  The
+# device code is the normal build's.  An object is rebuilt only when a source
+# or header is newer than it.
+SANITIZE_DIR = os.path.join(BUILD, "sanitize")
+SANITIZED_LIB = os.path.join(SANITIZE_DIR, "libpred_san.so")
+_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host",
+        "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _newest_input(src):
+    paths = [os.path.join(CSRC, src), os.path.join(INCLUDE, "pred.h"), os.path.join(CSRC, "common.h"),
+             os.path.join(CSRC, "kernels.h"), os.path.abspath(__file__)]
+    return max(os.path.getmtime(q) for q in paths)
+
+
+def _compile_host_sanitized(src):
+    obj = os.path.join(SANITIZE_DIR, src + ".o")
+    if os.path.exists(obj) and os.path.getmtime(obj) > _newest_input(src):
+        return obj
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), *_SAN, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build_host_sanitized(verbose=False):
+    """libpred with ASan + UBSan on its host code: load it with the sanitizer
+    runtime preloaded (the library links it as a shared runtime)."""
+    os.makedirs(SANITIZE_DIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(_compile_host_sanitized, SOURCES))
+    if not (os.path.exists(SANITIZED_LIB) and os.path.getmtime(SANITIZED_LIB) > max(map(os.path.getmtime, objs))):
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-fsanitize=address,undefined",
+               "-shared-libsan", "-o", SANITIZED_LIB, *objs]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {SANITIZED_LIB}")
+    return SANITIZED_LIB
+
+
+def sanitizer_runtime():
+    """Path of the ASan runtime the sanitized library links against (to preload)."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+        return path
+    import glob
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return found[-1] if found else None
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--host-sanitized" in sys.argv:
+        build_host_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)
