@@ -578,3 +578,137 @@ def test_forced_generic_row_scores():
         assert np.array_equal(np.isneginf(a), np.isneginf(g))
         m = ~np.isneginf(a)
         assert_scores(g[m], a[m], R, "generic row scores against the MFMA row scorer")
+
+
+# ------------------------------------------------- projections: correctly rounded at scale
+
+def _surely_rounded(q, P):
+    """Outputs where the oracle's float64 dot product, whatever its rounding error (at most
+    D * 2^-52 * sum|products|), is farther from both bf16 rounding midpoints around it than that
+    error: there the oracle's bf16 is the correctly rounded one, so the GPU must equal it bit for
+    bit.  The midpoints are halfway to the neighbouring bf16 values (ordinals +-1)."""
+    x = bf16.decode(q).reshape(-1, q.shape[-1])
+    p = bf16.decode(P)
+    y = x @ p
+    err = x.shape[1] * 2.0 ** -52 * (np.abs(x) @ np.abs(p))
+    o = bf16.ordinal(bf16.encode(y))
+
+    def from_ordinal(k):
+        k = np.clip(k, -0x7F80, 0x7F80)
+        return bf16.decode(np.where(k >= 0, k, 0x8000 | (-k)).astype(np.uint16))
+
+    v = from_ordinal(o)
+    lo_mid = (from_ordinal(o - 1) + v) / 2
+    hi_mid = (from_ordinal(o + 1) + v) / 2
+    with np.errstate(invalid="ignore"):
+        dist = np.minimum(np.abs(y - lo_mid), np.abs(hi_mid - y))
+    return np.isfinite(dist) & (dist > err)
+
+
+def _tie_projection(D, R, rng):
+    """P with P[j, j] = 1 and P[D/2 + j, j] = 2^-8 (0 elsewhere), and queries whose two
+    terms land every output exactly on a bf16 rounding midpoint or one ulp of float32 beside
+    it: ties to even and near-ties the bound cannot decide."""
+    P = np.zeros((D, R))
+    for j in range(R):
+        P[j, j] = 1.0
+        P[D // 2 + j, j] = 2.0 ** -8
+    return bf16.encode(P)
+
+
+@pytest.mark.parametrize("D,R,n_vec,kind", [(128, 64, 20000, "normal"), (128, 32, 40000, "normal"),
+                                            (64, 64, 17000, "cancel"), (128, 64, 16400, "ties"),
+                                            (256, 32, 33000, "normal"), (32, 64, 16500, "small"),
+                                            (128, 64, 16390, "nonfinite")])
+def test_project_q_large_calls_exact(D, R, n_vec, kind):
+    """Large project_q calls (>= 4096 16x16 output tiles: the streaming float64 MFMA kernel)
+    return the correctly rounded bf16 of the exact dot products bit for bit: on random data, on
+    cancelling pairs (outputs near zero with large sums of |products|), on exact rounding
+    midpoints and float32-near midpoints (ties to even), on values near the float32 subnormal
+    range, and with infinities and NaNs in the input."""
+    assert (n_vec + 15) // 16 * (R // 16) >= 4096
+    _say("project_q large call", D, R, n_vec, kind)
+    rng = np.random.default_rng(D * 7 + R + n_vec)
+    d = rk.dims(1, 1, 1, D, R, 16, 4)
+    if kind == "ties":
+        P = _tie_projection(D, R, rng)
+        qf = np.zeros((n_vec, D))
+        qf[:, :R] = rng.integers(1, 255, size=(n_vec, R)) * 2.0 ** -7 + 1.0     # 1 + k 2^-7: bf16-exact
+        qf[:, D // 2:D // 2 + R] = rng.choice([1.0, 3.0, 5.0, -1.0, 1.0 + 2 ** -7, 1.0 - 2 ** -8], size=(n_vec, R))
+        q = bf16.encode(qf).reshape(n_vec, 1, D)
+    else:
+        P = prng.projection(D, R, 777 + D + R)
+        if kind == "cancel":
+            # pairs of equal P rows and opposite query values: the sums cancel to small residuals
+            P = P.copy()
+            P[1::2] = P[0::2]
+            x = rng.standard_normal((n_vec, D // 2))
+            qf = np.empty((n_vec, D))
+            qf[:, 0::2] = x
+            qf[:, 1::2] = -x * (1.0 + rng.integers(-2, 3, size=x.shape) * 2.0 ** -7)
+            q = bf16.encode(qf).reshape(n_vec, 1, D)
+        elif kind == "small":
+            q = _randn_bits(rng, (n_vec, 1, D), 2.0 ** -60)        # products near 2^-120
+        else:
+            q = _randn_bits(rng, (n_vec, 1, D))
+            if kind == "nonfinite":
+                q = q.copy()
+                q[3, 0, 5] = 0x7F80      # +inf
+                q[700, 0, 9] = 0xFF80    # -inf
+                q[900, 0, 1] = 0x7FC0    # NaN
+                q[1500, 0, 7] = 0x7F7F   # largest finite: some sums overflow float32
+                q[1500, 0, 8] = 0x7F7F
+    with rk.Predictor(d, projection=P) as p:
+        qp = torch.empty((n_vec, 1, R), dtype=torch.bfloat16, device="cuda")
+        rk.pred_project_q(p.handle, _to_dev(q), qp)
+        torch.cuda.synchronize()
+        got = _bits_np(qp)
+    want = predictor.project_q(q, P)
+    if kind == "nonfinite":
+        # NaN outputs may carry any NaN payload; everything else exactly
+        gnan = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+        wnan = ((want & 0x7F80) == 0x7F80) & ((want & 0x7F) != 0)
+        assert np.array_equal(gnan, wnan)
+        assert np.array_equal(got[~gnan], want[~wnan])
+    elif kind == "ties":
+        # every term is a multiple of 2^-15 below 2^9: the oracle's float64 sums are exact
+        bad = got != want
+        assert not bad.any(), f"{int(bad.sum())} outputs differ; first at {np.argwhere(bad)[0]}"
+    else:
+        sure = _surely_rounded(q, P).reshape(got.shape)
+        assert sure.mean() > 0.99, sure.mean()
+        bad = (got != want) & sure
+        assert not bad.any(), f"{int(bad.sum())} outputs differ; first at {np.argwhere(bad)[0]}"
+        assert_ulp(got, want, "q_proj")   # and everywhere within the 1-ulp bar
+
+
+@pytest.mark.parametrize("R,B,Hk,n_blocks", [(64, 16, 8, 128), (32, 16, 8, 300), (64, 32, 4, 130)])
+def test_project_kv_block_large_calls_exact(R, B, Hk, n_blocks):
+    """Large project_kv_block calls (the prefill chunk's 128 new blocks) through the paged output
+    map: every slot equals the correctly rounded projection, slots go through the block table,
+    and an invalid entry is skipped and reported."""
+    D = 128
+    n_vec = n_blocks * B * Hk
+    assert (n_vec + 15) // 16 * (R // 16) >= 4096
+    _say("project_kv_block large call", R, B, Hk, n_blocks)
+    rng = np.random.default_rng(R + B + Hk + n_blocks)
+    N = n_blocks + 20
+    d = rk.dims(1, Hk, Hk, D, R, B, N)
+    with rk.Predictor(d, 4321 + R, flags=rk.PRED_FLAG_ZERO_AG) as p:
+        P = prng.projection(D, R, 4321 + R)
+        k = _randn_bits(rng, (1, n_blocks, B, Hk, D))
+        tab = rng.permutation(N)[:n_blocks].astype(np.int32)
+        bad = tab.copy()
+        bad[7] = N + 3
+        rk.pred_project_kv_block(p.handle, 0, _to_dev(k), _tab_dev(bad[None]))
+        with pytest.raises(rk.PredError) as e:
+            rk.pred_device_error(p.handle)
+        assert e.value.code == rk.PRED_ERR_DEVICE
+        want = predictor.project_kv_slots(k[0], P)
+        got = np.stack([rk.pred_read_slot(p.handle, 0, int(b)) for b in tab])
+        ok = np.ones(n_blocks, bool)
+        ok[7] = False
+        sure = _surely_rounded(k[0], P).reshape(n_blocks, B, Hk, R).transpose(0, 2, 1, 3)
+        assert ((got != want) & sure)[ok].sum() == 0
+        assert_ulp(got[ok], want[ok], "A_g")
+        assert not got[7].any()            # slot tab[7] was never written (A_g zeroed)
