@@ -27,7 +27,8 @@ MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, 2.5 PFLOP/s
 
 # sources of each score kernel family (the recorded counters hold only while these are unchanged)
 _KERNEL_SOURCES = {"score_decode": ["score_decode.hip", "common.h", "kernels.h"],
-                   "score_prefill": ["score_prefill.hip", "common.h", "kernels.h"]}
+                   "score_prefill": ["score_prefill.hip", "common.h", "kernels.h"],
+                   "score_rows": ["score_rows.hip", "common.h", "kernels.h"]}
 
 
 def _score_kernel_source_hash(family="score_decode"):
@@ -356,7 +357,8 @@ def main():
                      "select_keep_us": {"median": round(ts[len(ts) // 2] * 1e3, 2), "min": round(ts[0] * 1e3, 2),
                                         "max": round(ts[-1] * 1e3, 2)},
                      "roofline": {"bound": "mfma", "achieved": round(r_ach, 2), "peak": MFMA_BF16_PEAK_TFS,
-                                  "unit": "TFLOP/s", "frac": round(r_ach / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                                  "unit": "TFLOP/s", "frac": round(r_ach / MFMA_BF16_PEAK_TFS, 4),
+                                  "traffic": _traffic(c.name, "score_rows"),
                                   "kernel": "score_rows_kernel", "algorithmic_flops_per_launch": rflops}}
 
     # the same layers scored one per call (a per-layer decode loop), each layer in turn

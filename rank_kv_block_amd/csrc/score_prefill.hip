@@ -116,7 +116,24 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, Prefill
     // query chunk c -> registers (16-byte piece p: query row p / CPR, piece p % CPR)
     const uint16_t* qrows = a.qp + ((int64_t)l * a.S + s) * (int64_t)a.M * a.Hq * R;
     u32x4_t gq[PPT];
+    // When g divides the chunk, a piece's (row, head) advance by a fixed step
+    // per chunk: its offset is computed once and a whole chunk adds a constant.
+    const bool steady = kChunk % g == 0;
+    const int64_t chunk_step = steady ? (int64_t)(kChunk / g) * a.Hq * R : 0;
+    int64_t piece_off[PPT];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int e = (tid + 256 * i) / CPR;
+        piece_off[i] = steady ? ((int64_t)(e / g) * a.Hq + kv * g + e % g) * R + ((tid + 256 * i) % CPR) * 8 : 0;
+    }
     auto load_chunk = [&](int c) {
+        if (steady && (c + 1) * kChunk <= gm.n_eff) {
+#pragma unroll
+            for (int i = 0; i < PPT; ++i)
+                if (PIECES % 256 == 0 || tid + 256 * i < PIECES)
+                    gq[i] = *reinterpret_cast<const u32x4_t*>(qrows + c * chunk_step + piece_off[i]);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
             const int p = tid + 256 * i;
