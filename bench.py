@@ -167,9 +167,49 @@ def time_steps(wl, steps, warmup):
     return (t1 - t0) / steps, sorted(a.elapsed_time(b) for a, b in ev)
 
 
+def keep_set_timing(wl, stream):
+    """Per-row causal scores and keep sets of the first layer and sequence of a many-row
+    workload: each query row against the blocks complete at its position, then every row's
+    top-k; each entry point timed with HIP events on `stream`, median of 20."""
+    import torch
+    import rank_kv_block_amd as rk
+    c = wl.cfg
+    wl.keep_setup(64)
+    evr, evs_k = [], []
+    for i in range(20):
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        tab = None if wl.tables is None else wl.tables[0]
+        e0.record(stream)
+        rk.pred_score_rows(wl.h, 0, wl.q_proj[0, 0], c.first_pos, tab, c.n, wl.row_scores)
+        e1.record(stream)
+        rk.pred_select_keep(wl.h, wl.row_scores, c.first_pos, c.B, wl.topk, wl.keep, wl.keep_ws)
+        e2.record(stream)
+        evr.append((e0, e1))
+        evs_k.append((e1, e2))
+    torch.cuda.synchronize()
+    rk.pred_device_error(wl.h)
+    tr = sorted(a.elapsed_time(b) for a, b in evr)
+    ts = sorted(a.elapsed_time(b) for a, b in evs_k)
+    # algorithmic work: every complete (row, block) pair, all heads and tokens
+    pairs = sum(c.complete_blocks(i) for i in range(c.M))
+    rflops = 2.0 * pairs * c.B * c.Hq * c.R
+    r_med = tr[len(tr) // 2]
+    r_ach = rflops / (r_med * 1e-3) / 1e12
+    return {"rows": c.M, "blocks": c.n, "first_pos": c.first_pos, "topk": wl.topk,
+            "score_rows_us": {"median": round(r_med * 1e3, 2), "min": round(tr[0] * 1e3, 2),
+                              "max": round(tr[-1] * 1e3, 2)},
+            "select_keep_us": {"median": round(ts[len(ts) // 2] * 1e3, 2), "min": round(ts[0] * 1e3, 2),
+                               "max": round(ts[-1] * 1e3, 2)},
+            "roofline": {"bound": "mfma", "achieved": round(r_ach, 2), "peak": MFMA_BF16_PEAK_TFS,
+                         "unit": "TFLOP/s", "frac": round(r_ach / MFMA_BF16_PEAK_TFS, 4),
+                         "traffic": _traffic(c.name, "score_rows"),
+                         "kernel": "score_rows_kernel", "algorithmic_flops_per_launch": rflops}}
+
+
 def other_configs(names, steps, warmup):
     """Each other workload in turn, set up, timed as the headline one (whole step and score kernel)
     and freed: one entry per workload with its score kernel's roofline."""
+    import torch
     import rank_kv_block_amd as rk
     from rank_kv_block_amd.workloads import CONFIGS, Workload
     out = {}
@@ -196,6 +236,8 @@ def other_configs(names, steps, warmup):
                 "roofline": roofline_of(c, kernel, score_ms),
                 "setup_s": round(setup_s, 2),
             }
+            if c.M > 1:
+                out[name]["keep_sets"] = keep_set_timing(wl, torch.cuda.current_stream())
         finally:
             wl.close()
     return out
@@ -325,41 +367,8 @@ def main():
     del graph
     rk.pred_device_error(wl.h)
 
-    # per-row causal scores and keep sets of the first layer and sequence (many-row
-    # workloads): each query row against the blocks complete at its position, then
-    # every row's top-k; timed per entry point, median of 20
-    keep_sets = None
-    if c.M > 1:
-        wl.keep_setup(64)
-        evr, evs_k = [], []
-        for i in range(20):
-            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-            tab = None if wl.tables is None else wl.tables[0]
-            e0.record(stream)
-            rk.pred_score_rows(wl.h, 0, wl.q_proj[0, 0], c.first_pos, tab, c.n, wl.row_scores)
-            e1.record(stream)
-            rk.pred_select_keep(wl.h, wl.row_scores, c.first_pos, c.B, wl.topk, wl.keep, wl.keep_ws)
-            e2.record(stream)
-            evr.append((e0, e1))
-            evs_k.append((e1, e2))
-        torch.cuda.synchronize()
-        rk.pred_device_error(wl.h)
-        tr = sorted(a.elapsed_time(b) for a, b in evr)
-        ts = sorted(a.elapsed_time(b) for a, b in evs_k)
-        # algorithmic work: every complete (row, block) pair, all heads and tokens
-        pairs = sum(c.complete_blocks(i) for i in range(c.M))
-        rflops = 2.0 * pairs * c.B * c.Hq * c.R
-        r_med = tr[len(tr) // 2]
-        r_ach = rflops / (r_med * 1e-3) / 1e12
-        keep_sets = {"rows": c.M, "blocks": c.n, "first_pos": c.first_pos, "topk": wl.topk,
-                     "score_rows_us": {"median": round(r_med * 1e3, 2), "min": round(tr[0] * 1e3, 2),
-                                       "max": round(tr[-1] * 1e3, 2)},
-                     "select_keep_us": {"median": round(ts[len(ts) // 2] * 1e3, 2), "min": round(ts[0] * 1e3, 2),
-                                        "max": round(ts[-1] * 1e3, 2)},
-                     "roofline": {"bound": "mfma", "achieved": round(r_ach, 2), "peak": MFMA_BF16_PEAK_TFS,
-                                  "unit": "TFLOP/s", "frac": round(r_ach / MFMA_BF16_PEAK_TFS, 4),
-                                  "traffic": _traffic(c.name, "score_rows"),
-                                  "kernel": "score_rows_kernel", "algorithmic_flops_per_launch": rflops}}
+    # per-row causal scores and keep sets of the first layer and sequence (many-row workloads)
+    keep_sets = keep_set_timing(wl, stream) if c.M > 1 else None
 
     # the same layers scored one per call (a per-layer decode loop), each layer in turn
     per_layer = None
