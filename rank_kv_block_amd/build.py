@@ -25,8 +25,8 @@ SOURCES = ["pred_api.hip", "proj.hip", "score_decode.hip", "score_prefill.hip", 
 # the projection generator must be plain IEEE float64 arithmetic, one operation at a time
 EXTRA = {
     "prng.cpp": ["-ffp-contract=off", "-fno-fast-math"],
-    # MFMA results straight into VGPRs: the max epilogue then reads them without
-    # accumulator-register copies
+    # MFMA results straight into VGPRs (both MFMA scorers): the max epilogue then
+    # reads them without accumulator-register copies
     "score_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
     # The MFMA scorers take maxima of MFMA results.  Without NaN semantics fmaxf
     # is a plain v_max3_f32; with them every operand the compiler cannot prove
@@ -34,7 +34,7 @@ EXTRA = {
     # per element), and the NaN-propagating maximum (v_maximum3_f32) measured
     # slower than both.  These files write NaN only as integer bit patterns, and
     # a NaN product (a slot holding non-finite keys) gives an unspecified score.
-    "score_rows.hip": ["-fno-honor-nans"],
+    "score_rows.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
 }
 
 

@@ -9,49 +9,37 @@
 // complete(r) <= b < stride.  A complete block whose table entry is outside
 // [0, max_blocks) scores NaN and raises the device error word.
 //
-// Work split.  A workgroup has 8 waves; wave w serves kv head w % Hk and, when
-// there are fewer than 8 kv heads, the (w / Hk)-th of 8 / Hk key sub-ranges.
-// A key group is the workgroup's keys: 8 / Hk sub-ranges of KT tiles of 32
-// keys (consecutive tokens of consecutive blocks).  A wave keeps its keys of
-// its kv head as MFMA A operands in registers and, per row tile of 32 rows,
-// multiplies them by the queries of that kv head's g query heads, one head per
-// step: A_kv [32 keys, R] x Q_h^T [R, 32 rows] on v_mfma_f32_32x32x16_bf16 (f32
-// accumulation; a lane holds one query row and 16 keys of a tile: element i is
-// key (i / 4) * 8 + 4 * (lane / 32) + i % 4), and folds each product into the
-// running maxima of the tile's blocks.
+// Work split.  An item is (row range, key range): RR row tiles of 32 rows and
+// 8 x KT tiles of 32 keys (consecutive tokens of consecutive blocks).  A
+// workgroup of 8 waves takes a contiguous range of items; wave w owns the w-th
+// KT key tiles of the item's key range for every kv head in turn, so the 8
+// waves always work on the same kv head and the same query rows.  That makes
+// the query operands shareable: per pass (one kv head and up to GS of its
+// query heads) they are staged once in LDS for the whole workgroup, already in
+// the MFMA B-operand layout (1 KiB per row tile, head and k-step of 16: lane
+// (col, half) at byte 16 * lane holds row col's k-values st * 16 + half * 8 ..
+// + 8), written by direct buffer-to-LDS loads.  A wave keeps its keys of the
+// current kv head as MFMA A operands in registers and multiplies them by the
+// staged queries on v_mfma_f32_32x32x16_bf16 (f32 accumulation): A [32 keys, R]
+// x Q^T [R, 32 rows], where a lane holds one query row and 16 keys of a tile
+// (element i is key (i / 4) * 8 + 4 * (lane / 32) + i % 4), folded into that
+// row's running maxima of the tile's blocks.  The maxima run over every kv
+// head and query head of the item in registers, so a wave ends the item with
+// the final scores of its (row, block) cells: no reduction across waves.
 //
-// Each wave streams its own queries: per step it loads the next step's 32
-// query vectors with 16-byte coalesced reads into registers, multiplies the
-// current step's vectors from its private LDS buffer (padded rows, so the MFMA
-// operand reads are free of bank conflicts), then writes the next step's
-// vectors to its other private buffer.  No query stage is shared, so the waves
-// never wait for each other inside a row tile.  They meet once per row tile:
-// each wave's block maxima (lane halves combined) go to LDS, one barrier, and
-// the workgroup takes the max over kv heads and stores the row tile's scores
-// along rows.  The reduction buffer is double-buffered where LDS allows, so
-// that barrier is the only one.
+// Pipelining.  Stages and key sets are double-buffered: while a pass
+// multiplies, the next pass's queries load into the other LDS stage and, on a
+// pass that starts a kv head, the next kv head's keys load into the other
+// register set.  One barrier per pass.  Passes run back to back across items,
+// so an item's first keys and queries load during the previous item.
 //
-// Scheduling.  One workgroup per CU (two waves per SIMD), as many as the GPU
-// has CUs.  The rows are cut into up to 8 parts; workgroup i serves part
-// i % parts, so with 8 parts each XCD (which takes every 8th workgroup) serves
-// one part and its L2 holds that part's queries.  A part's work items --
-// (key group, row tile), key group major -- are split into equal contiguous
-// ranges over its workgroups; a wave reloads its keys only when the group
-// changes, and issues that load before the previous item's reduction so the
-// reduction hides part of its latency.  Key tiles past the row tile's last
+// Scheduling.  One workgroup per CU (the stages take most of the LDS), at
+// most as many as the GPU has CUs.  Items are numbered key range fastest and
+// split into equal contiguous ranges, so the workgroups of one XCD (every 8th)
+// share a few key ranges in their L2.  Key tiles past a row tile's last
 // complete block skip their MFMAs (their scores are -inf).
 #include "common.h"
 #include "kernels.h"
-
-// Tuning knobs (compile-time).
-// key registers per wave: KT = PRED_ROWS_KEY_REGS / (4 * R / 16) tiles, at most 8
-#ifndef PRED_ROWS_KEY_REGS
-#define PRED_ROWS_KEY_REGS 96
-#endif
-// row parts (an XCD's L2 holds one part's queries when there are 8)
-#ifndef PRED_ROWS_MAX_PARTS
-#define PRED_ROWS_MAX_PARTS 8
-#endif
 
 namespace pred {
 
@@ -59,15 +47,13 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kLdsBytes = 160 * 1024;
 
 struct RowGeom {
-    int wpk;              // waves per kv head: 8 / Hk key sub-ranges
-    int64_t groups;       // key groups (wpk * KT * 32 keys each)
-    int row_tiles;        // ceil(rows / 32)
-    int parts;            // row parts
-    int tiles_per_part;
-    int wg_per_part;      // workgroups serving each part
+    int64_t n_kr;     // key ranges
+    int64_t items;    // row ranges x key ranges
+    int gs;           // query heads per pass
+    int hp;           // passes per kv head
+    int wgs;          // workgroups
 };
 
 __device__ inline int64_t complete_blocks(const RowScoreArgs& a, int64_t r) {
@@ -75,268 +61,269 @@ __device__ inline int64_t complete_blocks(const RowScoreArgs& a, int64_t r) {
     return c < a.n ? c : a.n;
 }
 
-constexpr int kt_rows(int r) {
-    const int t = (PRED_ROWS_KEY_REGS / 4) / (r / 16);
-    return t < 1 ? 1 : (t > 8 ? 8 : t);
-}
-
+// Shape constants.  KT * RS = 16 (128 registers for two key sets), at most 8
+// tiles; RR row tiles keep the running maxima at 32 registers; GS query heads
+// fill a 64 KiB stage.
 template <int R, int BS>
-struct RowsLds {
-    static constexpr int KT = kt_rows(R);
-    static constexpr int ROWB = R * 2 + 16;                    // LDS bytes per query vector
-    static constexpr int BPT = 32 / BS;                        // blocks per key tile
-    static constexpr int NB = KT * BPT;                        // blocks of a wave's keys
-    static constexpr int NBP = NB | 1;                         // reduction row stride (odd: no bank conflicts)
-    static constexpr int STAGE = 32 * ROWB;                    // one head of one row tile
-    static constexpr int RED = kWaves * 32 * NBP * 4;          // one reduction buffer
-    static constexpr int NRED = (kWaves * 2 * STAGE + 2 * RED <= kLdsBytes) ? 2 : 1;
-    static_assert(kWaves * 2 * STAGE + RED <= kLdsBytes, "query stages and reduction exceed LDS");
+struct RowsCfg {
+    static constexpr int RS = R / 16;                              // MFMA k-steps of 16
+    static constexpr int KT = (16 / RS) < 8 ? 16 / RS : 8;         // key tiles per wave
+    static constexpr int BPT = 32 / BS;                            // blocks per key tile
+    static constexpr int NB = KT * BPT;                            // blocks of a wave
+    static constexpr int RR = (32 / NB) < 1 ? 1 : ((32 / NB) > 4 ? 4 : 32 / NB);   // row tiles per item
+    static constexpr int GS = 16 / RS;                             // query heads per stage
+    static constexpr int STAGE = RR * GS * RS * 1024;              // bytes of one stage
+    static constexpr int KEYS = kWaves * KT * 32;                  // keys per item
+    static_assert(2 * STAGE <= 160 * 1024, "stages exceed LDS");
 };
 
-// R: projected width; BS: block size.
 template <int R, int BS>
 __global__ __launch_bounds__(kThreads) void score_rows_kernel(RowScoreArgs a, RowGeom gm) {
-    using L = RowsLds<R, BS>;
-    constexpr int KT = L::KT;
-    constexpr int RS = R / 16;                        // MFMA k-steps of 16
-    constexpr int CPR = R / 8;                        // 16-byte pieces per query vector
-    constexpr int ROWB = L::ROWB;
-    constexpr int PPL = (32 * CPR) / 64;              // pieces per lane per step (>= 1 for R >= 16)
-    constexpr int BPT = L::BPT;
+    using C = RowsCfg<R, BS>;
+    constexpr int RS = C::RS, KT = C::KT, BPT = C::BPT, NB = C::NB, RR = C::RR, GS = C::GS;
     constexpr int EPB = BS / 2;                       // accumulator elements per block in a lane
-    constexpr int NB = L::NB;
-    constexpr int NRED = L::NRED;
-    __shared__ __attribute__((aligned(16))) unsigned char stage[kWaves][2][L::STAGE];
-    constexpr int NBP = L::NBP;
-    __shared__ float red[NRED][kWaves][32 * NBP];     // per wave: block maxima [row][block]
+    __shared__ __attribute__((aligned(1024))) unsigned char stage[2][C::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int kv = w % a.Hk;
-    const int sub = w / a.Hk;
-    const int g = a.Hq / a.Hk;
-    const int part = (int)(blockIdx.x % gm.parts);
-    const int jw = (int)(blockIdx.x / gm.parts);
-    const int t_first = part * gm.tiles_per_part;
-    const int nt = (gm.row_tiles - t_first) < gm.tiles_per_part ? (gm.row_tiles - t_first) : gm.tiles_per_part;
-    if (nt <= 0) return;   // whole workgroup
-    const int64_t items = gm.groups * nt;
-    const int64_t i_begin = items * jw / gm.wg_per_part;
-    const int64_t i_end = items * (jw + 1) / gm.wg_per_part;
-    if (i_begin >= i_end) return;   // whole workgroup
     const int col = lane & 31;      // key of a tile (A operand) / query row (B operand)
     const int half = lane >> 5;     // which 8 of the 16 k-values of one MFMA step
+    const int g = a.Hq / a.Hk;
+    const int64_t i_begin = gm.items * blockIdx.x / gm.wgs;
+    const int64_t i_end = gm.items * (blockIdx.x + 1) / gm.wgs;
+    if (i_begin >= i_end) return;   // whole workgroup
     const int64_t n_keys = a.n * BS;
     const int64_t slot_elems = (int64_t)a.Hk * BS * R;
     const uint32_t row_bytes = (uint32_t)a.Hq * R * 2;   // one query row, all heads
-    const uint32_t my_lds = (uint32_t)(uintptr_t)&stage[w][0][0];
+    const int epochs_per_item = a.Hk;                     // one epoch per kv head
+    const int64_t e_begin = i_begin * epochs_per_item;
+    const int64_t e_end = i_end * epochs_per_item;
 
-    // Per-lane constants of a step: piece i of the lane is query row p / CPR of
-    // the tile, 16-byte piece p % CPR (p = lane + 64 i): its byte offset from the
-    // tile's head-0 vector of row 0, and its LDS offset in a stage buffer.
-    uint32_t q_off[PPL], l_off[PPL];
-#pragma unroll
-    for (int i = 0; i < PPL; ++i) {
-        const int p = lane + 64 * i;
-        q_off[i] = (uint32_t)(p / CPR) * row_bytes + (uint32_t)(p % CPR) * 16;
-        l_off[i] = (uint32_t)((p / CPR) * ROWB + (p % CPR) * 16);
-    }
-    const uint32_t rd_off = (uint32_t)(col * ROWB + half * 16);   // MFMA operand read, k-step 0
-
-    // A operands: this lane's key of each of the wave's tiles in group grp
-    bf16x8_t kb[KT][RS];
-    auto load_keys = [&](int64_t grp) {
+    // A operands of one epoch (item, kv head): this lane's key of each of the
+    // wave's tiles.  Returns the wave's blocks whose table entry is invalid,
+    // bit t * BPT + bi for block bi of tile t.
+    auto load_keys = [&](bf16x8_t (&kb)[KT][RS], int64_t e) -> uint32_t {
+        const int64_t item = e / epochs_per_item;
+        const int kv = (int)(e - item * epochs_per_item);
+        const int64_t kr = item % gm.n_kr;
+        const int64_t key0 = kr * C::KEYS + (int64_t)w * (KT * 32) + col;
+        int64_t phys[KT];
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
-            const int64_t key = (grp * gm.wpk + sub) * (KT * 32) + t * 32 + col;
-            const uint16_t* src = a.ag;   // lanes without a valid key: in bounds; their blocks are never stored
-            if (key < n_keys) {
-                const int64_t b = key / BS;
-                const int tok = (int)(key - b * BS);
-                const int64_t phys = a.table ? (int64_t)a.table[b] : b;
-                if (phys >= 0 && phys < a.N)
-                    src = a.ag + (a.layer * a.N + phys) * slot_elems + ((int64_t)kv * BS + tok) * R;
-            }
+            const int64_t key = key0 + t * 32;
+            phys[t] = (key < n_keys ? key : n_keys - 1) / BS;
+        }
+        if (a.table) {   // every table read in flight at once
+#pragma unroll
+            for (int t = 0; t < KT; ++t) phys[t] = a.table[phys[t]];
+        }
+        uint32_t bad = 0;
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            const int64_t key = key0 + t * 32;
+            const bool live = key < n_keys;
+            const bool valid = phys[t] >= 0 && phys[t] < a.N;
+            const int tok = (int)(key % BS);
+            // lanes without a valid key read in bounds; their blocks are never stored as scores
+            const uint16_t* src =
+                live && valid ? a.ag + (a.layer * a.N + phys[t]) * slot_elems + ((int64_t)kv * BS + tok) * R : a.ag;
 #pragma unroll
             for (int st = 0; st < RS; ++st) kb[t][st] = load8(src + st * 16 + half * 8);
+            const uint64_t m = __ballot(live && !valid);
+#pragma unroll
+            for (int bi = 0; bi < BPT; ++bi)
+                if ((m >> (bi * BS)) & ((1ull << BS) - 1)) bad |= 1u << (t * BPT + bi);
+        }
+        return bad;
+    };
+
+    // Queries of one pass (epoch e, head group hg) into stage buffer sb: chunk
+    // (rt, j, st) of the stage is row tile rt, query head kv * g + hg * gs + j,
+    // k-step st; each wave loads every 8th chunk.  The buffer range ends at the
+    // item's last real row, so the padding rows of a partial tile read zeros.
+    auto load_stage = [&](int64_t e, int hg, int sb) {
+        const int64_t item = e / epochs_per_item;
+        const int kv = (int)(e - item * epochs_per_item);
+        const int64_t r0 = (item / gm.n_kr) * (RR * 32);
+        const int64_t left = a.rows - r0 < RR * 32 ? a.rows - r0 : RR * 32;
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(a.qp + r0 * a.Hq * R), (short)0, (int)((uint32_t)left * row_bytes), 0x00020000);
+        const int h0 = kv * g + hg * gm.gs;
+        const int ge = (g - hg * gm.gs) < gm.gs ? g - hg * gm.gs : gm.gs;
+        const uint32_t lane_off = (uint32_t)col * row_bytes + (uint32_t)half * 16;
+#pragma unroll
+        for (int i = 0; i < (RR * GS * RS + kWaves - 1) / kWaves; ++i) {
+            const int c = w + kWaves * i;
+            const int st = c % RS;
+            const int j = (c / RS) % GS;
+            const int rt = c / (RS * GS);
+            if (c < RR * GS * RS && j < ge)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc, (__attribute__((address_space(3))) void*)&stage[sb][c * 1024], 16,
+                    (int)(lane_off + (uint32_t)rt * 32 * row_bytes + st * 32), (h0 + j) * R * 2, 0, 0);
         }
     };
 
-    float rm[KT][BPT];
+    float rm[RR][KT][BPT];
 #pragma unroll
-    for (int t = 0; t < KT; ++t)
+    for (int rt = 0; rt < RR; ++rt)
 #pragma unroll
-        for (int bi = 0; bi < BPT; ++bi) rm[t][bi] = -__builtin_inff();
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int bi = 0; bi < BPT; ++bi) rm[rt][t][bi] = -__builtin_inff();
 
-    // query vectors of one step (row tile rt, head h) -> registers: buffer loads
-    // from the tile's first row, whose range ends at the last real row, so the
-    // padding rows of a partial tile read zeros (never stored)
-    u32x4_t gq[PPL];
-    auto fetch = [&](int rt, int h) {
-        const int64_t r0 = (int64_t)rt * 32;
-        const int64_t left = a.rows - r0 < 32 ? a.rows - r0 : 32;
-        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(a.qp + r0 * a.Hq * R), (short)0, (int)((uint32_t)left * row_bytes), 0x00020000);
-        const int soff = h * R * 2;
-#pragma unroll
-        for (int i = 0; i < PPL; ++i)
-            gq[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)q_off[i], soff, 0));
-    };
-    auto put = [&](int buf) {
-        const uint32_t base = my_lds + (uint32_t)(buf * L::STAGE);
-#pragma unroll
-        for (int i = 0; i < PPL; ++i)
-            *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(base + l_off[i]) = gq[i];
-    };
-    auto chain = [&](int t, const bf16x8_t (&qb)[RS]) {
+    auto chain = [&](const bf16x8_t (&kb)[KT][RS], int t, const bf16x8_t (&qb)[RS]) {
         f32x16_t acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[t][0], qb[0], f32x16_t{}, 0, 0, 0);
 #pragma unroll
         for (int st = 1; st < RS; ++st) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[t][st], qb[st], acc, 0, 0, 0);
         return acc;
     };
-    auto fold = [&](int t, const f32x16_t& acc) {
+    auto fold = [&](float (&m)[KT][BPT], int t, const f32x16_t& acc) {
 #pragma unroll
         for (int bi = 0; bi < BPT; ++bi) {
-            float m = rm[t][bi];
+            float v = m[t][bi];
 #pragma unroll
-            for (int e = 0; e < EPB; e += 2) m = fmaxf(fmaxf(m, acc[bi * EPB + e]), acc[bi * EPB + e + 1]);
-            rm[t][bi] = m;
+            for (int e = 0; e < EPB; e += 2) v = fmaxf(fmaxf(v, acc[bi * EPB + e]), acc[bi * EPB + e + 1]);
+            m[t][bi] = v;
         }
     };
-    // The wave's first ntl key tiles against the vectors in buffer buf.  With
+    // The wave's first ntl key tiles against one step's query operands.  With
     // every tile live, tile t + 1's chain is issued before tile t's fold, so the
     // fold's VALU work runs while the matrix core multiplies.
-    auto multiply = [&](int buf, int ntl) {
-        const uint32_t base = my_lds + (uint32_t)(buf * L::STAGE) + rd_off;
-        bf16x8_t qb[RS];
-#pragma unroll
-        for (int st = 0; st < RS; ++st)
-            qb[st] = __builtin_bit_cast(bf16x8_t,
-                                        *reinterpret_cast<__attribute__((address_space(3))) const u32x4_t*>(base + st * 32));
+    auto multiply = [&](const bf16x8_t (&kb)[KT][RS], const bf16x8_t (&qb)[RS], float (&m)[KT][BPT], int ntl) {
         if (ntl == KT) {
             f32x16_t acc[2];
-            acc[0] = chain(0, qb);
+            acc[0] = chain(kb, 0, qb);
 #pragma unroll
             for (int t = 1; t < KT; ++t) {
-                acc[t & 1] = chain(t, qb);
-                fold(t - 1, acc[(t - 1) & 1]);
+                acc[t & 1] = chain(kb, t, qb);
+                fold(m, t - 1, acc[(t - 1) & 1]);
             }
-            fold(KT - 1, acc[(KT - 1) & 1]);
+            fold(m, KT - 1, acc[(KT - 1) & 1]);
             return;
         }
 #pragma unroll
         for (int t = 0; t < KT; ++t)
-            if (t < ntl) fold(t, chain(t, qb));
+            if (t < ntl) fold(m, t, chain(kb, t, qb));
     };
 
-    // Stores of one row tile: entry i = tid + 512 j of the 32 x nbg (row, block)
-    // maxima, consecutive threads on consecutive blocks of a row; the max over
-    // the kv heads' partial maxima, -inf for an incomplete block, NaN for an
-    // invalid table entry.
-    const int nbg = gm.wpk * NB;   // blocks of a group
-    auto store_tile = [&](int rb, int64_t sgrp, int srt) {
-        const int64_t r0 = (int64_t)srt * 32;
-        const int64_t blk0 = sgrp * nbg;
-        for (int i = tid; i < nbg * 32; i += kThreads) {
-            const int row = i / nbg;
-            const int bw = i - row * nbg;
-            const int s2 = bw / NB;
-            const int blk = bw - s2 * NB;
-            const int64_t r = r0 + row;
-            const int64_t b = blk0 + bw;
-            if (r < a.rows && b < a.n) {
-                const bool complete = b < (a.first_pos + r + 1) / BS;
-                const int64_t phys = (complete && a.table) ? (int64_t)a.table[b] : 0;   // in flight during the reads
-                // the kv heads' partial maxima: all reads issued before the first is needed
-                const float* src = &red[rb][s2 * a.Hk][row * NBP + blk];
-                float part[kWaves];
+    // One pass over stage buffer sb: every row tile of the item against ge
+    // query heads, B operands read from LDS per step.
+    auto compute_pass = [&](const bf16x8_t (&kb)[KT][RS], int sb, int ge, const int (&ntl)[RR]) {
+        const uint32_t base = (uint32_t)(uintptr_t)&stage[sb][0] + (uint32_t)lane * 16;
 #pragma unroll
-                for (int k = 0; k < kWaves; ++k) part[k] = k < a.Hk ? src[k * 32 * NBP] : -__builtin_inff();
-                float v = part[0];
+        for (int rt = 0; rt < RR; ++rt) {
+            if (ntl[rt] == 0) continue;
+            for (int j = 0; j < ge; ++j) {
+                bf16x8_t qb[RS];
 #pragma unroll
-                for (int k = 1; k < kWaves; ++k) v = fmaxf(v, part[k]);
-                uint32_t bits = __float_as_uint(v);
-                if (!complete) {
-                    bits = 0xFF800000u;   // -inf
-                } else if (phys < 0 || phys >= a.N) {
-                    bits = 0x7FC00000u;   // NaN (as bits: this file is compiled without NaN semantics)
-                    atomicOr(a.err, DEVERR_TABLE);
+                for (int st = 0; st < RS; ++st)
+                    qb[st] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<__attribute__((address_space(3))) const u32x4_t*>(
+                                                              base + (uint32_t)(((rt * GS + j) * RS + st) * 1024)));
+                // the wave's MFMA stream issues ahead of the other wave's VALU and LDS work
+                __builtin_amdgcn_s_setprio(1);
+                multiply(kb, qb, rm[rt], ntl[rt]);
+                __builtin_amdgcn_s_setprio(0);
+            }
+        }
+    };
+
+    // Scores of the item ending with epoch e: the two lane halves hold
+    // different keys of the same row; after combining them, half h stores the
+    // wave's blocks h * NB / 2 .. of its row (consecutive floats along the
+    // row), -inf for an incomplete block, NaN for an invalid table entry.
+    auto store_item = [&](int64_t item, uint32_t bad) {
+        const int64_t r0 = (item / gm.n_kr) * (RR * 32);
+        const int64_t blk0 = ((item % gm.n_kr) * C::KEYS + (int64_t)w * (KT * 32)) / BS;
+#pragma unroll
+        for (int rt = 0; rt < RR; ++rt) {
+            const int64_t r = r0 + rt * 32 + col;
+            const int64_t cb = r < a.rows ? (a.first_pos + r + 1) / BS : 0;   // complete blocks of row r
+            float v[NB];
+#pragma unroll
+            for (int t = 0; t < KT; ++t)
+#pragma unroll
+                for (int bi = 0; bi < BPT; ++bi) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rm[rt][t][bi]),
+                                                                     __float_as_uint(rm[rt][t][bi]), false, false);
+                    v[t * BPT + bi] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                    rm[rt][t][bi] = -__builtin_inff();
                 }
-                reinterpret_cast<uint32_t*>(a.scores)[r * a.stride + b] = bits;
+            if (r < a.rows) {
+                uint32_t* out = reinterpret_cast<uint32_t*>(a.scores) + r * a.stride;
+#pragma unroll
+                for (int i = 0; i < (NB + 1) / 2; ++i) {
+                    const int k = half * ((NB + 1) / 2) + i;   // the wave's block index
+                    if (k < NB && blk0 + k < a.n) {
+                        uint32_t bits = __float_as_uint(v[k]);
+                        if (blk0 + k >= cb) {
+                            bits = 0xFF800000u;   // incomplete: -inf
+                        } else if ((bad >> k) & 1u) {
+                            bits = 0x7FC00000u;   // NaN (as bits: this file is compiled without NaN semantics)
+                            atomicOr(a.err, DEVERR_TABLE);
+                        }
+                        out[blk0 + k] = bits;
+                    }
+                }
             }
         }
     };
 
-    int64_t grp = i_begin / nt;
-    int rt = t_first + (int)(i_begin - grp * nt);
-    int buf = 0;
-    int red_buf = 0;
-    // the previous row tile, stored during this one's first step (two reduction buffers)
-    bool pending = false;
-    int64_t p_grp = 0;
-    int p_rt = 0;
-    load_keys(grp);
-    fetch(rt, kv * g);
-    put(0);
-    for (int64_t item = i_begin; item < i_end; ++item) {
-        const bool more = item + 1 < i_end;
-        const int n_rt = (rt + 1 - t_first) < nt ? rt + 1 : t_first;
-        const int64_t n_grp = n_rt == t_first ? grp + 1 : grp;
-        // key tiles holding a block complete for the row tile's last row
-        const int64_t last = ((int64_t)rt * 32 + 31) < a.rows ? ((int64_t)rt * 32 + 31) : a.rows - 1;
-        int64_t climit = (a.first_pos + last + 1) / BS;
-        if (climit > a.n) climit = a.n;
-        const int64_t key_first = (grp * gm.wpk + sub) * (KT * 32);
-        int ntl = 0;
+    // key tiles holding a block complete for each row tile's last row
+    auto live_tiles = [&](int64_t item, int (&ntl)[RR]) {
+        const int64_t r0 = (item / gm.n_kr) * (RR * 32);
+        const int64_t key_first = (item % gm.n_kr) * C::KEYS + (int64_t)w * (KT * 32);
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
-            if ((key_first + t * 32) / BS < climit) ntl = t + 1;
-        for (int hs = 0; hs < g; ++hs) {
-            // The next step's vectors are in flight during this step's MFMAs.  The
-            // fetch is unconditional (the last step re-reads its own vectors) so
-            // that on every path the newest loads are queries, and waiting for the
-            // keys never waits for them.
-            const bool last_step = hs + 1 == g;
-            fetch(last_step ? (more ? n_rt : rt) : rt, kv * g + (last_step ? (more ? 0 : hs) : hs + 1));
-            multiply(buf, ntl);
-            if (NRED == 2 && hs == 0 && pending) {
-                // the previous row tile's stores, while this step's MFMAs run
-                store_tile(red_buf ^ 1, p_grp, p_rt);
-                pending = false;
-            }
-            put(buf ^ 1);   // that buffer's vectors were read by the previous step
-            buf ^= 1;
+        for (int rt = 0; rt < RR; ++rt) {
+            const int64_t last = (r0 + rt * 32 + 31) < a.rows ? r0 + rt * 32 + 31 : a.rows - 1;
+            int64_t climit = (a.first_pos + last + 1) / BS;
+            if (climit > a.n) climit = a.n;
+            int n = 0;
+#pragma unroll
+            for (int t = 0; t < KT; ++t)
+                if ((key_first + t * 32) / BS < climit) n = t + 1;
+            ntl[rt] = r0 + rt * 32 < a.rows ? n : 0;
         }
-        // row tile done: the next group's keys first (their latency overlaps the reduction)
-        if (more && n_grp != grp) load_keys(n_grp);
-        float* rw = &red[red_buf][w][0];
-#pragma unroll
-        for (int t = 0; t < KT; ++t)
-#pragma unroll
-            for (int bi = 0; bi < BPT; ++bi) {
-                // rows 0..15 and 16..31 of each key sit in the two lane halves
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rm[t][bi]),
-                                                                 __float_as_uint(rm[t][bi]), false, false);
-                if (half == 0) rw[col * NBP + t * BPT + bi] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-                rm[t][bi] = -__builtin_inff();
+    };
+
+    // One epoch (item, kv head) with its keys in kc; the next epoch's keys go
+    // to kn.  Passes alternate the stage buffers (pass parity sb).
+    int sb = 0;
+    uint32_t bad_cur = 0, bad_next = 0;
+    int ntl[RR];
+    auto epoch = [&](bf16x8_t (&kc)[KT][RS], bf16x8_t (&kn)[KT][RS], int64_t e) {
+        const int64_t item = e / epochs_per_item;
+        const int kv = (int)(e - item * epochs_per_item);
+        if (kv == 0) live_tiles(item, ntl);
+        for (int hg = 0; hg < gm.hp; ++hg) {
+            // this pass's queries (and keys) have landed for every wave, and
+            // every wave is done with the other stage buffer
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (hg == 0 && e + 1 < e_end) {
+                const uint32_t b = load_keys(kn, e + 1);
+                if ((e + 1) % epochs_per_item == 0) bad_next = b;
             }
-        // every wave's maxima of this row tile are in LDS; every wave has also
-        // finished the previous row tile's stores, so its buffer is free again
-        __syncthreads();
-        if constexpr (NRED == 2) {
-            pending = true;
-            p_grp = grp;
-            p_rt = rt;
-            red_buf ^= 1;
-        } else {
-            store_tile(0, grp, rt);
-            __syncthreads();   // the buffer is written again next row tile
+            if (hg + 1 < gm.hp) load_stage(e, hg + 1, sb ^ 1);
+            else if (e + 1 < e_end) load_stage(e + 1, 0, sb ^ 1);
+            const int ge = (g - hg * gm.gs) < gm.gs ? g - hg * gm.gs : gm.gs;
+            compute_pass(kc, sb, ge, ntl);
+            sb ^= 1;
         }
-        grp = n_grp;
-        rt = n_rt;
+        if (kv + 1 == epochs_per_item) {
+            store_item(item, bad_cur);
+            bad_cur = bad_next;
+        }
+    };
+
+    bf16x8_t k0[KT][RS], k1[KT][RS];
+    bad_cur = load_keys(k0, e_begin);
+    load_stage(e_begin, 0, 0);
+    for (int64_t e = e_begin; e < e_end; e += 2) {
+        epoch(k0, k1, e);
+        if (e + 1 < e_end) epoch(k1, k0, e + 1);
     }
-    if (pending) store_tile(red_buf ^ 1, p_grp, p_rt);
 }
 
 // Any shape: one thread per (row, column of the stride), f32 dot products.
@@ -384,23 +371,18 @@ __global__ __launch_bounds__(256) void fill_tail_cols_kernel(float* scores, int6
 
 template <int R, int BS>
 hipError_t launch_rk(const RowScoreArgs& a, hipStream_t st) {
-    constexpr int KT = RowsLds<R, BS>::KT;
+    using C = RowsCfg<R, BS>;
     RowGeom gm;
-    gm.wpk = kWaves / a.Hk;
     const int64_t n_keys = a.n * BS;
-    const int64_t keys_per_group = (int64_t)gm.wpk * KT * 32;
-    gm.groups = (n_keys + keys_per_group - 1) / keys_per_group;
-    gm.row_tiles = (int)((a.rows + 31) / 32);
-    int parts = PRED_ROWS_MAX_PARTS;
-    while (parts > 1 && parts > gm.row_tiles) parts >>= 1;
-    gm.tiles_per_part = (gm.row_tiles + parts - 1) / parts;
-    gm.parts = (gm.row_tiles + gm.tiles_per_part - 1) / gm.tiles_per_part;   // no empty parts
-    const int64_t items_per_part = gm.groups * gm.tiles_per_part;
-    int64_t wpp = (a.n_cu > 0 ? a.n_cu : 256) / gm.parts;
-    if (wpp < 1) wpp = 1;
-    if (wpp > items_per_part) wpp = items_per_part;
-    gm.wg_per_part = (int)wpp;
-    const int64_t wgs = (int64_t)gm.parts * wpp;
+    gm.n_kr = (n_keys + C::KEYS - 1) / C::KEYS;
+    const int64_t n_rr = (a.rows + C::RR * 32 - 1) / (C::RR * 32);
+    gm.items = n_rr * gm.n_kr;
+    const int g = a.Hq / a.Hk;
+    gm.gs = g < C::GS ? g : C::GS;
+    gm.hp = (g + gm.gs - 1) / gm.gs;
+    int64_t wgs = a.n_cu > 0 ? a.n_cu : 256;
+    if (wgs > gm.items) wgs = gm.items;
+    gm.wgs = (int)wgs;
     if (!grid_fits(wgs)) return hipErrorInvalidConfiguration;
     score_rows_kernel<R, BS><<<(unsigned)wgs, kThreads, 0, st>>>(a, gm);
     return hipGetLastError();
