@@ -116,6 +116,58 @@ def test_score_rows_parity(shape):
             _check_keep_sets(keep.cpu().numpy(), got, want, first_pos, B, topk, R, f"keep {shape} k={topk}")
 
 
+# Shapes with hundreds of (row range, key range) work items, so that every
+# workgroup of the MFMA scorer runs several items back to back: items that end
+# and start inside one workgroup, the next item's keys and queries loaded during
+# the previous one, items with no complete block at all, and (Hk = 1) a key set
+# per item.  One table entry is invalid: its block scores NaN in every row that
+# has it complete.
+MANY_ITEM_SHAPES = [
+    # Hq, Hk, D, R, B, N, n, rows, first_pos
+    (8, 1, 64, 64, 16, 700, 640, 10000, 3000),     # 128-row items, one kv head
+    (32, 8, 64, 32, 16, 1100, 1000, 6000, 0),      # 64-row items, most key ranges beyond every row
+    (16, 4, 64, 64, 16, 600, 520, 9000, 2000),     # 128-row items, four kv heads
+]
+
+
+@pytest.mark.parametrize("shape", MANY_ITEM_SHAPES)
+def test_score_rows_many_items(shape):
+    Hq, Hk, D, R, B, N, n, rows, first_pos = shape
+    _say("score_rows many items", shape)
+    rng = np.random.default_rng(sum((i + 3) * v for i, v in enumerate(shape)))
+    d = rk.dims(1, Hq, Hk, D, R, B, N)
+    with rk.Predictor(d, 11 + R) as p:
+        phys = rng.permutation(N)[:n].astype(np.int32)
+        k = _randn_bits(rng, (1, n, B, Hk, D))
+        rk.pred_project_kv_block(p.handle, 0, _to_dev(k).view(torch.bfloat16),
+                                 torch.from_numpy(phys.reshape(1, n)).cuda())
+        bad = 5
+        tab_host = phys.copy()
+        tab_host[bad] = N + 3                       # outside [0, N)
+        q = _randn_bits(rng, (rows, Hq, R))
+        sc = torch.full((rows, n), 12345.0, dtype=torch.float32, device="cuda")
+        rk.pred_score_rows(p.handle, 0, _to_dev(q).view(torch.bfloat16), first_pos,
+                           torch.from_numpy(tab_host).cuda(), n, sc)
+        got = sc.cpu().numpy()
+        with pytest.raises(rk.PredError) as e:
+            rk.pred_device_error(p.handle)
+        assert e.value.code == rk.PRED_ERR_DEVICE
+        # the causal mask on every row, the invalid block's NaN wherever it is complete
+        cnt = np.minimum(n, (first_pos + np.arange(rows) + 1) // B)
+        col = np.arange(n)[None, :]
+        assert np.array_equal(np.isneginf(got), col >= cnt[:, None]), "-inf exactly past each row's count"
+        has_bad = cnt > bad
+        assert np.isnan(got[has_bad, bad]).all() and not np.isnan(np.delete(got, bad, axis=1)).any()
+        # sampled rows against the oracle (the invalid block left out)
+        slots = a_g_layer(p.handle, d, 0)[phys]
+        sample = sorted(set(rng.choice(rows, 48, replace=False).tolist()) | {0, rows - 1, rows // 2})
+        for i in sample:
+            want = predictor.score_rows(q[i:i + 1], slots, first_pos + i, n)[0]
+            m = np.isfinite(want)
+            m[bad] = False
+            assert_scores(got[i][m], want[m], R, f"many items, row {i}")
+
+
 def test_score_rows_edge_cases():
     """No blocks, no complete block for any row, one row, and an invalid table entry (NaN + error)."""
     d = rk.dims(1, 8, 2, 32, 32, 16, 16)
