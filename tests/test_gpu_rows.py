@@ -73,15 +73,15 @@ def _check_keep_sets(keep, gpu_scores, oracle_scores, first_pos, ratio, topk, r,
 
 ROW_SHAPES = [
     # Hq, Hk, D, R, B, N, n, rows, first_pos, stride, table         path
-    (32, 8, 64, 32, 16, 40, 40, 70, 500, 40, "perm"),             # mfma, 2 kv heads per wave, every block complete late on
+    (32, 8, 64, 32, 16, 40, 40, 70, 500, 40, "perm"),             # mfma, r 32: 8 key tiles per wave, 64-row items
     (32, 8, 64, 32, 16, 40, 37, 45, 0, 43, "perm"),               # mfma, causal from position 0, tail columns
-    (8, 2, 64, 64, 8, 96, 90, 100, 640, 90, "identity"),          # mfma, two waves per kv head, B 8
-    (4, 4, 32, 16, 32, 20, 20, 33, 37, 25, "identity"),           # mfma, B 32, one head per wave
-    (8, 1, 64, 128, 16, 24, 24, 64, 200, 24, "perm"),             # mfma, R 128, one kv head for all waves
-    (16, 8, 64, 128, 16, 20, 20, 40, 300, 20, "perm"),            # mfma, R 128 with 2 kv heads per wave
-    (24, 8, 64, 32, 8, 30, 30, 50, 120, 30, "identity"),          # mfma, 6 heads per wave over 2 kv heads
-    (64, 8, 64, 64, 32, 12, 12, 40, 300, 12, "identity"),         # mfma, g 8, 16 heads per wave
-    (6, 1, 64, 16, 8, 30, 30, 31, 100, 28, "perm"),               # plain kernel (Hq not a multiple of 4), stride < n
+    (8, 2, 64, 64, 8, 96, 90, 100, 640, 90, "identity"),          # mfma, B 8: 4 blocks per key tile
+    (4, 4, 32, 16, 32, 20, 20, 33, 37, 25, "identity"),           # mfma, r 16, B 32, one query head per kv head
+    (8, 1, 64, 128, 16, 24, 24, 64, 200, 24, "perm"),             # mfma, r 128, g 8: four passes per kv head
+    (16, 8, 64, 128, 16, 20, 20, 40, 300, 20, "perm"),            # mfma, r 128, g 2
+    (24, 8, 64, 32, 8, 30, 30, 50, 120, 30, "identity"),          # mfma, g 3 (a pass of 3 heads), 32-row items
+    (64, 8, 64, 64, 32, 12, 12, 40, 300, 12, "identity"),         # mfma, g 8: two passes per kv head
+    (6, 1, 64, 16, 8, 30, 30, 31, 100, 28, "perm"),               # mfma, g 6, r 16, B 8 (32-row items), stride < n
     (6, 3, 32, 16, 16, 20, 20, 40, 100, 22, "perm"),              # plain kernel (Hk 3)
     (4, 2, 32, 24, 16, 20, 20, 40, 250, 20, "identity"),          # plain kernel (R 24)
 ]
