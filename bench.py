@@ -206,9 +206,12 @@ def keep_set_timing(wl, stream):
                          "kernel": "score_rows_kernel", "algorithmic_flops_per_launch": rflops}}
 
 
-def other_configs(names, steps, warmup):
-    """Each other workload in turn, set up, timed as the headline one (whole step and score kernel)
-    and freed: one entry per workload with its score kernel's roofline."""
+def other_configs(names, steps, warmup, keep_alive):
+    """Each other workload in turn, set up and timed as the headline one (whole step and score
+    kernel): one entry per workload with its score kernel's roofline.  Workloads are freed only
+    after all are timed (appended to keep_alive): freeing device memory starts the driver's
+    clearing of it in the background, which measurably slows a memory-bound kernel timed right
+    after (the batched decode step by ~3%)."""
     import torch
     import rank_kv_block_amd as rk
     from rank_kv_block_amd.workloads import CONFIGS, Workload
@@ -218,28 +221,26 @@ def other_configs(names, steps, warmup):
         print(f"[bench] config {name}: {c.description}", file=sys.stderr, flush=True)
         t_setup = time.perf_counter()
         wl = Workload(c)
+        keep_alive.append(wl)
         setup_s = time.perf_counter() - t_setup
-        try:
-            step_s, each = time_steps(wl, steps, warmup)
-            kernel = rk.pred_score_kernel_name(wl.h, c.M)
-            score_ms = sum(each) / len(each)
-            a_g_bytes = c.blocks_per_step * c.slot_bytes
-            out[name] = {
-                "description": c.description,
-                "a_g_bytes_per_step": a_g_bytes,
-                "ms_per_step": round(step_s * 1e3, 4),
-                "step_a_g_gbs": round(a_g_bytes / step_s / 1e9, 2),
-                "blocks_per_s": round(c.blocks_per_step / step_s, 1),
-                "score_kernel_us": {"mean": round(score_ms * 1e3, 2), "median": round(each[len(each) // 2] * 1e3, 2),
-                                    "min": round(each[0] * 1e3, 2), "max": round(each[-1] * 1e3, 2)},
-                "score_kernel_variant": rk.pred_score_kernel_variant(wl.h, c.M, c.n),
-                "roofline": roofline_of(c, kernel, score_ms),
-                "setup_s": round(setup_s, 2),
-            }
-            if c.M > 1:
-                out[name]["keep_sets"] = keep_set_timing(wl, torch.cuda.current_stream())
-        finally:
-            wl.close()
+        step_s, each = time_steps(wl, steps, warmup)
+        kernel = rk.pred_score_kernel_name(wl.h, c.M)
+        score_ms = sum(each) / len(each)
+        a_g_bytes = c.blocks_per_step * c.slot_bytes
+        out[name] = {
+            "description": c.description,
+            "a_g_bytes_per_step": a_g_bytes,
+            "ms_per_step": round(step_s * 1e3, 4),
+            "step_a_g_gbs": round(a_g_bytes / step_s / 1e9, 2),
+            "blocks_per_s": round(c.blocks_per_step / step_s, 1),
+            "score_kernel_us": {"mean": round(score_ms * 1e3, 2), "median": round(each[len(each) // 2] * 1e3, 2),
+                                "min": round(each[0] * 1e3, 2), "max": round(each[-1] * 1e3, 2)},
+            "score_kernel_variant": rk.pred_score_kernel_variant(wl.h, c.M, c.n),
+            "roofline": roofline_of(c, kernel, score_ms),
+            "setup_s": round(setup_s, 2),
+        }
+        if c.M > 1:
+            out[name]["keep_sets"] = keep_set_timing(wl, torch.cuda.current_stream())
     return out
 
 
@@ -429,10 +430,12 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
-    wl.close()
     others = [n for n in args.configs.split(",") if n and n != "none" and n != c.name]
+    alive = [wl]
     if others:
-        out["configs"] = other_configs(others, args.config_steps, min(args.warmup, 3))
+        out["configs"] = other_configs(others, args.config_steps, min(args.warmup, 3), alive)
+    for w in alive:
+        w.close()
     del side
     torch.cuda.synchronize()
     # this process starts no other process; say so from the process table at the end
