@@ -209,9 +209,9 @@ def keep_set_timing(wl, stream):
 def other_configs(names, steps, warmup, keep_alive):
     """Each other workload in turn, set up and timed as the headline one (whole step and score
     kernel): one entry per workload with its score kernel's roofline.  Workloads are freed only
-    after all are timed (appended to keep_alive): freeing device memory starts the driver's
-    clearing of it in the background, which measurably slows a memory-bound kernel timed right
-    after (the batched decode step by ~3%)."""
+    after all are timed (appended to keep_alive): after a large free, a memory-bound kernel timed
+    within the next seconds runs measurably slower (the batched decode step by ~3%; 25 s of idle
+    restores it), most likely the driver clearing the freed memory in the background."""
     import torch
     import rank_kv_block_amd as rk
     from rank_kv_block_amd.workloads import CONFIGS, Workload
