@@ -178,6 +178,15 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, Prefill
             for (int i = 0; i < 16; i += 2) m = fmaxf(fmaxf(m, acc[t][i]), acc[t][i + 1]);
             rm[t] = m;
         }
+        // Schedule: two MFMAs, then the max instructions that match them (8
+        // max3 per key tile against RS MFMAs), repeated, so the max of one key
+        // tile issues between the next tiles' MFMAs instead of after all of
+        // them (r = 64: 2.5% faster than the compiler's own order)
+#pragma unroll
+        for (int i = 0; i < NKT * RS / 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);          // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 16 / RS, 0);    // VALU
+        }
     };
 
     load_chunk(c_begin);
