@@ -181,6 +181,7 @@ void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
     Off voff[NS];
     uint32_t soff_slot[NS];   // UNI: the whole slot offset is wave-uniform (SGPR)
     uint32_t live = 0;
+    uint32_t okbits = 0;      // slot sl's block has a valid table entry (the stores reuse it)
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl) {
         const int f = sl * 64 + lane;
@@ -195,6 +196,7 @@ void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
         soff_slot[sl] = (uint32_t)((ok ? (int64_t)phys : 0) * slot_elems * 2 + 1024 * (sl % gm.SPB));
         const bool cut = b_first + bi == a.n - 1 && t >= fill_s;
         live |= ((ok && !cut) ? 1u : 0u) << sl;
+        okbits |= (ok ? 1u : 0u) << sl;
     }
 
     float rm[NS];
@@ -309,12 +311,11 @@ void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
 
     // Block maxima and stores.
     float* out = a.scores + ((int64_t)l * a.S + s) * a.n;
-    const int32_t* table = a.tables ? a.tables + (int64_t)s * a.n : nullptr;
-    auto store = [&](int bi, float v) {
+    // slot sl holds block bi for the storing lane; its table check was made at set-up
+    auto store = [&](int bi, int sl, float v) {
         const int64_t b = b_first + bi;
         if (bi < gm.NBW && b < a.n) {
-            const int64_t phys = table ? (int64_t)table[b] : b;
-            if (phys >= 0 && phys < a.N) {
+            if ((okbits >> sl) & 1u) {
                 out[b] = v;
             } else {
                 out[b] = __uint_as_float(0x7FC00000u);
@@ -331,7 +332,7 @@ void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
             acc = fmaxf(acc, rm[sl]);
             if ((sl + 1) % gm.SPB == 0) {
                 const float v = wave_max_xor(acc, 64);
-                if (lane == 0) store(sl / gm.SPB, v);
+                if (lane == 0) store(sl / gm.SPB, sl, v);
                 acc = -__builtin_inff();
             }
         }
@@ -340,7 +341,7 @@ void score_decode_kernel(ScoreArgs a, DecodeGeom gm) {
         for (int sl = 0; sl < NS; ++sl) {
             const float v = wave_max_xor(rm[sl], gm.U);
             const int f = sl * 64 + lane;
-            if ((lane & (gm.U - 1)) == 0) store(f >> gm.log2U, v);
+            if ((lane & (gm.U - 1)) == 0) store(f >> gm.log2U, sl, v);
         }
     }
 }
