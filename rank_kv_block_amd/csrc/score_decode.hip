@@ -397,6 +397,7 @@ __global__ __launch_bounds__(256) void score_decode_mfma_kernel(ScoreArgs a, Dec
     // (sl % SPB) * 16 / H ..).  live: TPL bits per slot, token 4c/H + v scored.
     uint32_t soff_slot[NS];
     uint64_t live = 0;
+    uint32_t okbits = 0;   // slot sl's block has a valid table entry (the stores reuse it)
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl) {
         const int bi = (sl * 64) >> gm.log2U;
@@ -412,6 +413,7 @@ __global__ __launch_bounds__(256) void score_decode_mfma_kernel(ScoreArgs a, Dec
             bits |= ((ok && !(last && tok >= fill_s)) ? 1u : 0u) << v;
         }
         live |= (uint64_t)bits << (4 * sl);
+        okbits |= (ok ? 1u : 0u) << sl;
     }
     float rm[NS];
 #pragma unroll
@@ -485,10 +487,9 @@ __global__ __launch_bounds__(256) void score_decode_mfma_kernel(ScoreArgs a, Dec
     }
 
     float* out = a.scores + ((int64_t)l * a.S + s) * a.n;
-    const int32_t* table = a.tables ? a.tables + (int64_t)s * a.n : nullptr;
-    auto store = [&](int64_t b, float v) {
-        const int64_t phys = table ? (int64_t)table[b] : b;
-        if (phys >= 0 && phys < a.N) {
+    // slot sl holds block b; its table check was made at set-up
+    auto store = [&](int64_t b, int sl, float v) {
+        if ((okbits >> sl) & 1u) {
             out[b] = v;
         } else {
             out[b] = __uint_as_float(0x7FC00000u);
@@ -508,7 +509,7 @@ __global__ __launch_bounds__(256) void score_decode_mfma_kernel(ScoreArgs a, Dec
             float v = half_max[wave_id];
 #pragma unroll
             for (int w = 1; w < WPB; ++w) v = fmaxf(v, half_max[wave_id + w]);
-            store(b_first, v);
+            store(b_first, 0, v);
         }
         return;
     } else {
@@ -520,7 +521,7 @@ __global__ __launch_bounds__(256) void score_decode_mfma_kernel(ScoreArgs a, Dec
                 const float v = wave_max_xor(acc, 64);
                 const int bi = sl / gm.SPB;
                 const int64_t b = b_first + bi;
-                if (lane == 0 && bi < gm.NBW && b < a.n) store(b, v);
+                if (lane == 0 && bi < gm.NBW && b < a.n) store(b, sl, v);
                 acc = -__builtin_inff();
             }
         }
