@@ -239,7 +239,7 @@ def other_configs(names, steps, warmup, keep_alive):
             "roofline": roofline_of(c, kernel, score_ms),
             "setup_s": round(setup_s, 2),
         }
-        if a_g_bytes < (64 << 20):
+        if a_g_bytes < (1 << 20) and kernel != "score_prefill_kernel":
             # a few KiB per call: launch latency, not a bandwidth or matrix roofline
             out[name]["roofline"] = {"bound": "launch latency", "score_call_us": round(score_ms * 1e3, 2),
                                      "kernel": kernel, "algorithmic_bytes_per_launch": a_g_bytes}
