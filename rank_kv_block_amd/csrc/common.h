@@ -66,6 +66,19 @@ __device__ inline uint32_t order_key(float x) {
     return (u & 0x80000000u) ? ~u : (u ^ 0x80000000u);
 }
 
+// Float max of v into the float at p, on its bit pattern: non-negative floats
+// order as signed integers, negative ones in reverse as unsigned integers, so
+// an integer max (v >= 0) or min (v < 0) is the float max.  A score starts at
+// -inf (0xFF800000), the identity of both.  The quiet NaN 0x7FC00000, stored
+// with the integer max, stays once stored: as a signed integer it is above
+// every finite or infinite non-negative pattern, and as an unsigned integer
+// above every negative one.
+__device__ inline void atomic_max_bits(uint32_t* p, float v) {
+    const uint32_t u = __float_as_uint(v);
+    if ((int32_t)u >= 0) atomicMax(reinterpret_cast<int*>(p), (int)u);
+    else atomicMin(p, u);
+}
+
 // MFMA operand and accumulator types (v_mfma_f32_32x32x16_bf16).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));

@@ -51,16 +51,6 @@ struct PrefillGeom {
     int64_t groups;       // key groups per (layer, sequence, kv head)
 };
 
-// Float max of v into the float at p, on its bit pattern: non-negative floats
-// order as signed integers, negative ones in reverse as unsigned integers, so
-// an integer max (v >= 0) or min (v < 0) is the float max.  A score starts at
-// -inf (0xFF800000), the identity of both.
-__device__ inline void atomic_max_bits(uint32_t* p, float v) {
-    const uint32_t u = __float_as_uint(v);
-    if ((int32_t)u >= 0) atomicMax(reinterpret_cast<int*>(p), (int)u);
-    else atomicMin(p, u);
-}
-
 // R: projected width; NKT: 32-key tiles per wave; BS: block size in tokens.
 template <int R, int NKT, int BS>
 __global__ __launch_bounds__(256) void score_prefill_kernel(ScoreArgs a, PrefillGeom gm, uint32_t* __restrict__ bits) {

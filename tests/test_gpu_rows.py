@@ -73,16 +73,16 @@ def _check_keep_sets(keep, gpu_scores, oracle_scores, first_pos, ratio, topk, r,
 
 ROW_SHAPES = [
     # Hq, Hk, D, R, B, N, n, rows, first_pos, stride, table         path
-    (32, 8, 64, 32, 16, 40, 40, 70, 500, 40, "perm"),             # mfma, r 32: 8 key tiles per wave, 64-row items
-    (32, 8, 64, 32, 16, 40, 37, 45, 0, 43, "perm"),               # mfma, causal from position 0, tail columns
-    (8, 2, 64, 64, 8, 96, 90, 100, 640, 90, "identity"),          # mfma, B 8: 4 blocks per key tile
+    (32, 8, 64, 32, 16, 40, 40, 70, 500, 40, "perm"),             # mfma, r 32: three row parts, the last chunk partial
+    (32, 8, 64, 32, 16, 40, 37, 45, 0, 43, "perm"),               # mfma, causal from position 0, ragged key group, tail columns
+    (8, 2, 64, 64, 8, 96, 90, 100, 640, 90, "identity"),          # mfma, B 8: 4 blocks per key tile, 64 per group
     (4, 4, 32, 16, 32, 20, 20, 33, 37, 25, "identity"),           # mfma, r 16, B 32, one query head per kv head
-    (8, 1, 64, 128, 16, 24, 24, 64, 200, 24, "perm"),             # mfma, r 128, g 8: four passes per kv head
+    (8, 1, 64, 128, 16, 24, 24, 64, 200, 24, "perm"),             # mfma, r 128, g 8: four stages per chunk
     (16, 8, 64, 128, 16, 20, 20, 40, 300, 20, "perm"),            # mfma, r 128, g 2
-    (24, 8, 64, 32, 8, 30, 30, 50, 120, 30, "identity"),          # mfma, g 3 (a pass of 3 heads), 32-row items
-    (64, 8, 64, 64, 32, 12, 12, 40, 300, 12, "identity"),         # mfma, g 8: two passes per kv head
-    (6, 1, 64, 16, 8, 30, 30, 31, 100, 28, "perm"),               # mfma, g 6, r 16, B 8 (32-row items), stride < n
-    (6, 3, 32, 16, 16, 20, 20, 40, 100, 22, "perm"),              # plain kernel (Hk 3)
+    (24, 8, 64, 32, 8, 30, 30, 50, 120, 30, "identity"),          # mfma, g 3: stages of 3 of up to 8 heads
+    (64, 8, 64, 64, 32, 12, 12, 40, 300, 12, "identity"),         # mfma, g 8: two stages per chunk
+    (6, 1, 64, 16, 8, 30, 30, 31, 100, 28, "perm"),               # mfma, g 6, r 16, B 8, stride < n
+    (6, 3, 32, 16, 16, 20, 20, 40, 100, 22, "perm"),              # mfma, Hk 3
     (4, 2, 32, 24, 16, 20, 20, 40, 250, 20, "identity"),          # plain kernel (R 24)
 ]
 
@@ -116,17 +116,16 @@ def test_score_rows_parity(shape):
             _check_keep_sets(keep.cpu().numpy(), got, want, first_pos, B, topk, R, f"keep {shape} k={topk}")
 
 
-# Shapes with hundreds of (row range, key range) work items, so that every
-# workgroup of the MFMA scorer runs several items back to back: items that end
-# and start inside one workgroup, the next item's keys and queries loaded during
-# the previous one, items with no complete block at all, and (Hk = 1) a key set
-# per item.  One table entry is invalid: its block scores NaN in every row that
-# has it complete.
+# Shapes where every workgroup of the MFMA scorer (one kv head, one key group,
+# one row part) runs dozens of 32-row chunks back to back, each chunk's maxima
+# reaching the scores by atomics while the next chunk multiplies, with several
+# row parts per key group and a shorter last part.  One table entry is invalid:
+# its block scores NaN in every row that has it complete.
 MANY_ITEM_SHAPES = [
     # Hq, Hk, D, R, B, N, n, rows, first_pos
-    (8, 1, 64, 64, 16, 700, 640, 10000, 3000),     # 128-row items, one kv head
-    (32, 8, 64, 32, 16, 1100, 1000, 6000, 0),      # 64-row items, most key ranges beyond every row
-    (16, 4, 64, 64, 16, 600, 520, 9000, 2000),     # 128-row items, four kv heads
+    (8, 1, 64, 64, 16, 700, 640, 10000, 3000),     # one kv head, g 8 (two stages per chunk), 25 row parts
+    (32, 8, 64, 32, 16, 1100, 1000, 6000, 0),      # most key groups past every row's complete count
+    (16, 4, 64, 64, 16, 600, 520, 9000, 2000),     # four kv heads, 8 row parts of 36 chunks
 ]
 
 
@@ -166,6 +165,45 @@ def test_score_rows_many_items(shape):
             m = np.isfinite(want)
             m[bad] = False
             assert_scores(got[i][m], want[m], R, f"many items, row {i}")
+
+
+def test_score_rows_signs():
+    """Scores of both signs: the kv heads of a cell meet through an integer max on the
+    bit pattern for non-negative scores and an integer min for negative ones.  Every
+    key of a block is close to +u or -u (u one projected key), every query close to
+    +u, so every block's score has the block's sign in every row, and kv head k's
+    keys are scaled by 1 + k / 4, so the heads disagree on each cell's value."""
+    Hq, Hk, D, R, B, N, n, rows, first_pos, stride = 8, 4, 64, 32, 8, 80, 70, 100, 300, 72
+    _say("score_rows signs", (Hq, Hk, D, R, B, N, n, rows, first_pos, stride))
+    rng = np.random.default_rng(17)
+    d = rk.dims(1, Hq, Hk, D, R, B, N)
+    with rk.Predictor(d, 23) as p:
+        phys = rng.permutation(N)[:n].astype(np.int32)
+        v = rng.standard_normal(D)
+        sign = np.where(np.arange(n) % 3 == 0, -1.0, 1.0)            # a third of the blocks negative
+        scale = 1.0 + np.arange(Hk) / 4.0
+        k = (sign[:, None, None, None] * scale[None, None, :, None] * v[None, None, None, :]
+             + 0.01 * rng.standard_normal((n, B, Hk, D)))
+        k_bits = bf16.encode(k.reshape(1, n, B, Hk, D))
+        rk.pred_project_kv_block(p.handle, 0, _to_dev(k_bits).view(torch.bfloat16),
+                                 torch.from_numpy(phys.reshape(1, n)).cuda())
+        slots = a_g_layer(p.handle, d, 0)[phys]                      # [n, Hk, B, R] bits
+        u = bf16.decode(slots[1, 0, 0])                              # block 1 is positive, kv head 0
+        q = bf16.encode(u[None, None, :] * (1.0 + 0.05 * rng.standard_normal((rows, Hq, R))))
+        sc = torch.full((rows, stride), 12345.0, dtype=torch.float32, device="cuda")
+        rk.pred_score_rows(p.handle, 0, _to_dev(q).view(torch.bfloat16), first_pos,
+                           torch.from_numpy(phys).cuda(), n, sc)
+        got = sc.cpu().numpy()
+        rk.pred_device_error(p.handle)
+        want = predictor.score_rows(q, slots, first_pos, stride)
+        masked = np.isneginf(want)
+        assert np.array_equal(np.isneginf(got), masked), "-inf exactly where a block is not complete"
+        fin = ~masked
+        neg_cols = np.zeros(stride, dtype=bool)
+        neg_cols[:n] = sign < 0
+        neg = fin & neg_cols[None, :]
+        assert (want[neg] < 0).all() and (want[fin & ~neg] > 0).all() and neg.sum() > 500
+        assert_scores(got[fin], want[fin], R, "score_rows signs")
 
 
 def test_score_rows_edge_cases():
