@@ -30,7 +30,7 @@ def _to_dev(bits):
 
 def _tab_dev(ids):
     """Block ids -> device int32 tensor."""
-    return torch.from_numpy(np.array(ids, dtype=np.int32)).cuda()   # a writable copy
+    return torch.from_numpy(np.array(ids, dtype=np.int32, order="C")).cuda()   # a writable contiguous copy
 
 
 def _read_slots(h, d, pairs):
