@@ -326,9 +326,36 @@ __global__ __launch_bounds__(kThreads) void score_rows_kernel(RowScoreArgs a, Ro
     flush(rc_end - 1);
 }
 
+// -inf into n floats: VEC threads write 4 floats each with one 16-byte store
+// (p 16-byte aligned), the last thread the ragged end.
+template <bool VEC>
 __global__ __launch_bounds__(256) void fill_neg_inf_kernel(uint32_t* p, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) p[i] = 0xFF800000u;
+    constexpr uint32_t kNegInf = 0xFF800000u;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if constexpr (VEC) {
+        const int64_t i = t * 4;
+        if (i + 4 <= n) {
+            *reinterpret_cast<u32x4_t*>(p + i) = u32x4_t{kNegInf, kNegInf, kNegInf, kNegInf};
+        } else {
+            for (int64_t k = i; k < n; ++k) p[k] = kNegInf;
+        }
+    } else {
+        if (t < n) p[t] = kNegInf;
+    }
+}
+
+hipError_t fill_neg_inf(float* scores, int64_t n, hipStream_t st) {
+    uint32_t* p = reinterpret_cast<uint32_t*>(scores);
+    if ((reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+        const int64_t blocks = ((n + 3) / 4 + 255) / 256;
+        if (!grid_fits(blocks)) return hipErrorInvalidConfiguration;
+        fill_neg_inf_kernel<true><<<(unsigned)blocks, 256, 0, st>>>(p, n);
+    } else {
+        const int64_t blocks = (n + 255) / 256;
+        if (!grid_fits(blocks)) return hipErrorInvalidConfiguration;
+        fill_neg_inf_kernel<false><<<(unsigned)blocks, 256, 0, st>>>(p, n);
+    }
+    return hipSuccess;
 }
 
 // Any shape: one thread per (row, column of the stride), f32 dot products.
@@ -389,9 +416,9 @@ hipError_t launch_rk(const RowScoreArgs& a, hipStream_t st) {
     gm.chunks_per_part = (int)cpp;
     const int64_t parts = (n_chunks + cpp - 1) / cpp;   // no empty parts
     const int64_t wgs = (int64_t)a.Hk * gm.groups * parts;
-    const int64_t cells = a.rows * a.stride;
-    if (!grid_fits(wgs) || !grid_fits((cells + 255) / 256)) return hipErrorInvalidConfiguration;
-    fill_neg_inf_kernel<<<(unsigned)((cells + 255) / 256), 256, 0, st>>>(reinterpret_cast<uint32_t*>(a.scores), cells);
+    if (!grid_fits(wgs)) return hipErrorInvalidConfiguration;
+    const hipError_t e = fill_neg_inf(a.scores, a.rows * a.stride, st);
+    if (e != hipSuccess) return e;
     score_rows_kernel<R, NKT, BS><<<(unsigned)wgs, kThreads, 0, st>>>(a, gm);
     return hipGetLastError();
 }

@@ -226,6 +226,19 @@ def test_score_rows_edge_cases():
         got = sc1.cpu().numpy()
         assert np.isfinite(got[0, :5]).all() and np.isneginf(got[0, 5:]).all()
         assert np.all(got[0, :5] == 0.0)   # A_g zeroed
+        _say("score_rows into an output that is not 16-byte aligned")
+        k = _to_dev(_randn_bits(rng, (1, 9, 16, 2, 32))).view(torch.bfloat16)
+        rk.pred_project_kv_block(p.handle, 0, k, torch.arange(9, dtype=torch.int32, device="cuda").view(1, 9))
+        aligned = torch.zeros((40, 9), dtype=torch.float32, device="cuda")
+        rk.pred_score_rows(p.handle, 0, q, 100, None, 9, aligned)
+        big = torch.full((41, 9), 7.0, dtype=torch.float32, device="cuda")
+        view = big[1:]                                   # starts 36 bytes into the allocation
+        assert view.data_ptr() % 16 != 0
+        rk.pred_score_rows(p.handle, 0, q, 100, None, 9, view)
+        assert torch.equal(view.cpu(), aligned.cpu()) and torch.all(big[0] == 7.0)
+        got = aligned.cpu().numpy()
+        cnt = np.minimum(9, (100 + np.arange(40) + 1) // 16)
+        assert np.array_equal(np.isneginf(got), np.arange(9)[None, :] >= cnt[:, None])
         _say("score_rows invalid table entry")
         tab = torch.tensor([0, 1, 99, 3], dtype=torch.int32, device="cuda")
         sc = torch.zeros((4, 4), dtype=torch.float32, device="cuda")
