@@ -30,10 +30,21 @@ __host__ __device__ inline uint64_t f64_bits(double x) {
 // bits shifted out.  The biased bf16 pattern is then ((qe + 133) << 7) + n,
 // which also carries a rounding overflow of n = 256 into the exponent and gives
 // the subnormal encoding when qe = -133.
+//
+// Values in bf16's normal range (2^-126 <= |x| < 2^128) take a shorter route
+// with the same result: there the quantum is the float64 significand's bit 45,
+// so adding 2^44 - 1 plus bit 45 (half-even) and dropping 45 bits rounds the
+// 7-bit fraction in place, a carry moving into the exponent; subtracting
+// (1023 - 127) << 7 rebiases the exponent (a carry up to 2^128 lands exactly on
+// the infinity pattern).
 __host__ __device__ inline uint16_t f64_to_bf16_rne(double x) {
     const uint64_t b = f64_bits(x);
     const uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
     const uint64_t a = b & 0x7FFFFFFFFFFFFFFFull;
+    if (a - 0x3810000000000000ull < 0x47F0000000000000ull - 0x3810000000000000ull) {
+        const uint64_t r = (a + 0x00000FFFFFFFFFFFull + ((a >> 45) & 1ull)) >> 45;
+        return (uint16_t)(sign | ((uint32_t)r - (896u << 7)));
+    }
     if (a > 0x7FF0000000000000ull) return 0x7FC0;     // NaN
     const int biased = (int)(a >> 52);
     if (biased == 0) return (uint16_t)sign;            // zero / float64 subnormal -> +/-0

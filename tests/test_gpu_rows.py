@@ -81,6 +81,7 @@ ROW_SHAPES = [
     (16, 8, 64, 128, 16, 20, 20, 40, 300, 20, "perm"),            # mfma, r 128, g 2
     (24, 8, 64, 32, 8, 30, 30, 50, 120, 30, "identity"),          # mfma, g 3: stages of 3 of up to 8 heads
     (64, 8, 64, 64, 32, 12, 12, 40, 300, 12, "identity"),         # mfma, g 8: two stages per chunk
+    (12, 2, 64, 64, 16, 30, 30, 70, 200, 30, "perm"),             # mfma, g 6: a full stage of 4 heads, then one of 2
     (6, 1, 64, 16, 8, 30, 30, 31, 100, 28, "perm"),               # mfma, g 6, r 16, B 8, stride < n
     (6, 3, 32, 16, 16, 20, 20, 40, 100, 22, "perm"),              # mfma, Hk 3
     (4, 2, 32, 24, 16, 20, 20, 40, 250, 20, "identity"),          # plain kernel (R 24)
