@@ -271,16 +271,23 @@ __global__ __launch_bounds__(kThreads) void score_rows_kernel(RowScoreArgs a, Ro
         for (int i = 0; i < NB / 2; ++i) sl[i] = half ? v[NB / 2 + i] : v[i];
     };
     // The slot of chunk rc to the scores: cell i = tid + kThreads * k is row
-    // i / NBG, block fb of the group.
+    // i / NBG, block fb of the group.  Per thread: its first row, its block's
+    // first complete row (block fblk is complete at row r iff r >= r_cmp) and
+    // its score address in row 0; a chunk and a k step add uniform offsets.
+    constexpr int RPK = kThreads / NBG;   // rows between a thread's cells
+    const int row0 = tid / NBG;
+    const int64_t r_cmp = (fblk + 1) * BS - 1 - a.first_pos;
+    uint32_t* const p_thread = reinterpret_cast<uint32_t*>(a.scores) + (int64_t)row0 * a.stride + fblk;
     auto flush = [&](int64_t rc) {
         if (fblk >= a.n) return;
         const float* sl = &slot[rc & 1][0];
+        uint32_t* const p_chunk = p_thread + rc * 32 * a.stride;
 #pragma unroll
         for (int k = 0; k < 32 * NBG / kThreads; ++k) {
-            const int row = (tid + kThreads * k) / NBG;
+            const int row = row0 + RPK * k;
             const int64_t r = rc * 32 + row;
-            if (r < a.rows && fblk < (a.first_pos + r + 1) / BS) {
-                uint32_t* p = reinterpret_cast<uint32_t*>(a.scores + r * a.stride + fblk);
+            if (r < a.rows && r >= r_cmp) {
+                uint32_t* p = p_chunk + (int64_t)(RPK * k) * a.stride;
                 if (fbad) {
                     atomicMax(reinterpret_cast<int*>(p), 0x7FC00000);   // NaN (as bits: no NaN semantics here)
                     atomicOr(a.err, DEVERR_TABLE);
