@@ -58,6 +58,9 @@ __device__ inline int64_t complete_blocks(const RowScoreArgs& a, int64_t r) {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+// s_waitcnt immediate (gfx9 encoding) for "every vector memory access done":
+// vmcnt 0 (bits 3:0 and 15:14), expcnt 7 and lgkmcnt 15 (bits 6:4, 11:8: no wait)
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 struct RowGeom {
     int64_t groups;        // key groups per kv head
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void score_rows_kernel(RowScoreArgs a, Ro
     // every path into the loop: otherwise the compiler keeps the key loads
     // pending at the loop header, and the waits it places before the
     // multiplies would also wait for each stage's own prefetch.
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     for (int64_t rc = rc_begin; rc < rc_end; ++rc) {
         for (int hg = 0; hg < gm.hp; ++hg) {
             __syncthreads();
