@@ -142,7 +142,12 @@ def roofline_of(c, kernel, score_ms):
 
 def time_steps(wl, steps, warmup):
     """Warm up, then time `steps` whole steps (project_step + score_blocks + rank_victims) on
-    torch's current stream: host wall time per step, and each score launch's HIP-event time (ms)."""
+    torch's current stream: host wall time per step, the HIP-event time (ms) of the score launch
+    of every `stride`-th step (every 4th from 32 steps, every 2nd from 16), and the stride.  A
+    timed event pair costs its step ~6 us of GPU idle (measured on the 8B step: 339-343 us with a pair
+    on every step, 335.5 with one on every 4th, 333.5 with none; the score kernel's own time
+    is the same either way), so bracketing every step would put the measurement into the
+    step time it measures."""
     import torch
     import rank_kv_block_amd as rk
     c = wl.cfg
@@ -151,20 +156,25 @@ def time_steps(wl, steps, warmup):
         wl.step(wl.layer0_for_step(i))
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    stride = 4 if steps >= 32 else (2 if steps >= 16 else 1)
+    ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for i in range(0, steps, stride)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         l0 = wl.layer0_for_step(i)
         rk.pred_project_step(wl.h, l0, wl.k_new[l0:l0 + nl], wl.table_new[l0:l0 + nl], wl.q[l0:l0 + nl], wl.q_proj)
-        ev[i][0].record(stream)
+        pair = ev.get(i)
+        if pair is not None:
+            pair[0].record(stream)
         rk.pred_score_blocks(wl.h, l0, wl.q_proj, wl.tables, wl.scores)
-        ev[i][1].record(stream)
+        if pair is not None:
+            pair[1].record(stream)
         rk.pred_rank_victims(wl.h, wl.scores.view(nl * c.S, c.n), wl.victims, wl.workspace)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     rk.pred_device_error(wl.h)
-    return (t1 - t0) / steps, sorted(a.elapsed_time(b) for a, b in ev)
+    return (t1 - t0) / steps, sorted(a.elapsed_time(b) for a, b in ev.values()), stride
 
 
 def keep_set_timing(wl, stream):
@@ -223,7 +233,7 @@ def other_configs(names, steps, warmup, keep_alive):
         wl = Workload(c)
         keep_alive.append(wl)
         setup_s = time.perf_counter() - t_setup
-        step_s, each = time_steps(wl, steps, warmup)
+        step_s, each, stride = time_steps(wl, steps, warmup)
         kernel = rk.pred_score_kernel_name(wl.h, c.M)
         score_ms = sum(each) / len(each)
         a_g_bytes = c.blocks_per_step * c.slot_bytes
@@ -234,7 +244,8 @@ def other_configs(names, steps, warmup, keep_alive):
             "step_a_g_gbs": round(a_g_bytes / step_s / 1e9, 2),
             "blocks_per_s": round(c.blocks_per_step / step_s, 1),
             "score_kernel_us": {"mean": round(score_ms * 1e3, 2), "median": round(each[len(each) // 2] * 1e3, 2),
-                                "min": round(each[0] * 1e3, 2), "max": round(each[-1] * 1e3, 2)},
+                                "min": round(each[0] * 1e3, 2), "max": round(each[-1] * 1e3, 2),
+                                "launches_timed": len(each), "of_every_nth_step": stride},
             "score_kernel_variant": rk.pred_score_kernel_variant(wl.h, c.M, c.n),
             "roofline": roofline_of(c, kernel, score_ms),
             "setup_s": round(setup_s, 2),
@@ -261,7 +272,7 @@ def main():
     ap.add_argument("--configs", default="tiny,batched_decode,long_context_70b,prefill_chunk",
                     help="other workloads timed after the headline one, in the same process (comma list, or "
                          "'none')")
-    ap.add_argument("--config-steps", type=int, default=20, help="timed steps of each other workload")
+    ap.add_argument("--config-steps", type=int, default=40, help="timed steps of each other workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -290,8 +301,8 @@ def main():
     stream = torch.cuda.current_stream()
     nl = c.step_layers
     print(f"[bench] warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
-    step_s, score_each = time_steps(wl, args.steps, args.warmup)
-    score_ms = sum(score_each) / args.steps
+    step_s, score_each, ev_stride = time_steps(wl, args.steps, args.warmup)
+    score_ms = sum(score_each) / len(score_each)
 
     # per-call breakdown of a step, in a separate loop so the timed steps above
     # carry no extra events: median of 20 steps per entry point
@@ -418,7 +429,8 @@ def main():
         "pct_hbm_peak_step": round(100.0 * a_g_bytes / step_s / 1e9 / HBM_PEAK_GBS, 2),
         "score_kernel_ms": round(score_ms, 4),
         "score_kernel_us": {"median": round(score_each[len(score_each) // 2] * 1e3, 2),
-                            "min": round(score_each[0] * 1e3, 2), "max": round(score_each[-1] * 1e3, 2)},
+                            "min": round(score_each[0] * 1e3, 2), "max": round(score_each[-1] * 1e3, 2),
+                            "launches_timed": len(score_each), "of_every_nth_step": ev_stride},
         "score_kernel_path": kernel,
         "score_kernel_variant": rk.pred_score_kernel_variant(wl.h, c.M, c.n),
         "roofline": roofline,
